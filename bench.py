@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the MegaMoE expert layer on one MI355X.
+
+One step = one full forward (dispatch -> L1 grouped GEMM + SwiGLU/re-quant -> L2 grouped GEMM
+-> combine) over one batch of seeded synthetic inputs that are resident in HBM before the
+timed region starts.  Default workload: the decode shape T=128, H=7168, I=2048, 256 experts,
+top-8 uniform routing, FP8 E4M3 with float scales per 128 (the shape the headline metric is
+quoted on).  Other shapes: --config 0..4.
+
+Prints one JSON line with the layer throughput (algorithmic TFLOP/s, 6*H*I flops per routed
+pair), the weight-stream rate, the dominant kernel's roofline fraction (per-kernel durations
+from HIP events recorded on the library's stream) and, on rank 0 at N=1, the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
+PHASES = ("dispatch", "l1_gemm_swiglu", "l2_gemm", "combine")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        h = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, h):
+        self.lib.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def weight_bytes_per_expert(spec):
+    H, I = spec.H, spec.I
+    if spec.recipe == 0:
+        l1 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+        l2 = H * I + (H // 128) * (I // 128) * 4
+    else:
+        l1 = 2 * I * H // 2 + 2 * I * (H // 32)
+        l2 = H * I // 2 + H * (I // 32)
+    return l1, l2
+
+
+def algorithmic_bytes(spec, touched, P):
+    """Bytes the method must move per call, per kernel (inputs read once, outputs written once)."""
+    H, I, T, k = spec.H, spec.I, spec.T, spec.k
+    l1w, l2w = weight_bytes_per_expert(spec)
+    xs = T * H + (T * (H // 128) * 4 if spec.recipe == 0 else T * (H // 32))
+    inter = P * I + (P * (I // 128) * 4 if spec.recipe == 0 else P * (I // 32))
+    return dict(
+        dispatch=T * k * 8 + P * 12,
+        l1_gemm_swiglu=touched * l1w + xs + P * 4 + inter,
+        l2_gemm=touched * l2w + inter + P * H * 2,
+        combine=P * H * 2 + T * H * 2,
+        weights=touched * (l1w + l2w),
+        io=xs + T * k * 8 + T * H * 2,
+    )
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(spec, P_dev, n_tokens):
+    """The oracle (as it stands) on the first n_tokens tokens of the same workload."""
+    import numpy as np
+
+    import oracle
+    idx = P_dev["topk_idx"][:n_tokens].cpu().numpy()
+    experts = sorted(set(int(e) for e in idx.reshape(-1) if 0 <= e < spec.E))
+
+    class HostExperts:
+        def __init__(self, t):
+            self.d = {e: t[e].cpu().numpy() for e in experts}
+
+        def __getitem__(self, e):
+            return self.d[e]
+
+    host = {k: HostExperts(P_dev[k]) for k in ("l1_w", "l1_sf", "l2_w", "l2_sf")}
+    for k in ("x", "x_sf", "topk_idx", "topk_w"):
+        host[k] = P_dev[k].cpu().numpy()
+    prob = oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp)
+    tokens = np.arange(n_tokens)
+    t0 = time.perf_counter()
+    oracle.forward(prob, tokens=tokens, **host)
+    dt = time.perf_counter() - t0
+    pairs = int(((idx >= 0) & (idx < spec.E)).sum())
+    return dict(value=6.0 * spec.H * spec.I * pairs / dt / 1e12, unit="TFLOP/s", cores=blas_threads(),
+                kind="oracle",
+                sample=f"first {n_tokens} of {spec.T} tokens ({pairs} routed pairs, {len(experts)} experts), "
+                       f"{dt:.1f} s, numpy float64 block sums")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
+    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path only: every expert is resident in one GPU's "
+              "HBM and the layer runs without collectives; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dispatch_fp8_grouped_topk_amd as mm
+    import synth
+
+    spec = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = synth.make_weights(spec, dev)
+    idx, w = synth.make_routing(spec)
+    x, x_sf = synth.make_activations(spec, dev)
+    P.update(x=x, x_sf=x_sf, topk_idx=idx.to(dev), topk_w=w.to(dev))
+    prob = mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, args.flags)
+    ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device=dev)
+    y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], P["l1_sf"], P["l2_w"], P["l2_sf"], y, ws)
+
+    for _ in range(args.warmup):
+        mm.mega_moe_forward(*call, stream=stream)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(mm.NUM_PHASE_EVENTS)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mm.mega_moe_forward_profiled(*call, events=evs[i], stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    phase_ms = {ph: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, ph in enumerate(PHASES)}
+    gpu_ms = float(np.mean([hip.elapsed_ms(e[0], e[-1]) for e in evs]))
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+
+    idx_np = idx.numpy()
+    valid = (idx_np >= 0) & (idx_np < spec.E)
+    pairs = int(valid.sum())
+    touched = int((np.bincount(idx_np[valid], minlength=spec.E) > 0).sum())
+    flops = 6.0 * spec.H * spec.I * pairs
+    ab = algorithmic_bytes(spec, touched, pairs)
+    sec = ms_step * 1e-3
+    dom = max(("l1_gemm_swiglu", "l2_gemm"), key=lambda p: phase_ms[p])
+    dom_gbps = ab[dom] / (phase_ms[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "MoE-layer TFLOP/s + weight GB/s vs roofline, H7168 I2048 256e top8",
+        "value": round(flops / sec / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if spec.recipe == 0 else "fp8_e4m3 x fp4_e2m1",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, quantised to the layer's formats)",
+        "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
+                   "recipe": "fp8_b128" if spec.recipe == 0 else "mxfp4w_b32", "routing": spec.routing,
+                   "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
+        "weight_GBps": round(ab["weights"] / sec / 1e9, 1),
+        "tokens_per_s": round(spec.T / sec, 1),
+        "hbm_frac_weights": round(ab["weights"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "mfma_frac": round(flops / sec / 1e12 / FP8_PEAK_TFLOPS, 5),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": ab[dom]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, P, min(args.cpu_tokens, spec.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,251 @@
+"""Python binding of libmegamoe, the MI355X (gfx950) MegaMoE expert-layer library.
+
+Argument marshalling only: torch tensors are passed to the C ABI (include/mega_moe.h) as raw
+device pointers together with the current HIP stream; every step of the layer runs in the
+library's HIP kernels.  There is no fallback: if the shared library is missing or fails to
+load, importing the binding's functions raises.
+
+Functions carry the C names:
+
+    mega_moe_workspace_size(problem) -> int
+    mega_moe_forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
+                     workspace, stream=None)
+    mega_moe_workspace_views(problem, workspace) -> dict of torch views into the workspace
+    mega_moe_strerror(status) -> str
+    mega_moe_abi_version() -> int
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmegamoe.so")
+
+RECIPE_FP8_B128 = 0
+RECIPE_MXFP4W_B32 = 1
+FLAG_TILE_AUTO = 0
+FLAG_TILE_SMALL = 1
+FLAG_TILE_LARGE = 2
+
+ABI_VERSION = 1
+
+
+class MegaMoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {mega_moe_strerror(status)} (status {status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """mega_moe_problem."""
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("recipe", ctypes.c_int32),
+        ("swiglu_clamp", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+    @classmethod
+    def make(cls, T, H, I, E, k, recipe=RECIPE_FP8_B128, swiglu_clamp=0.0, flags=0):
+        return cls(int(T), int(H), int(I), int(E), int(k), int(recipe), float(swiglu_clamp), int(flags))
+
+
+class _Views(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("expert_count", "expert_offset", "pool_src", "pair_pos", "num_invalid",
+                 "inter_q", "inter_sf", "slot")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m dispatch_fp8_grouped_topk_amd.build`")
+    # torch first: its HIP runtime (soname libamdhip64.so.7) is then the one the library binds
+    # to, so torch streams and the library's launches share one runtime.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp = ctypes.c_void_p
+    lib.mega_moe_abi_version.restype = ctypes.c_int
+    lib.mega_moe_abi_version.argtypes = []
+    lib.mega_moe_strerror.restype = ctypes.c_char_p
+    lib.mega_moe_strerror.argtypes = [ctypes.c_int]
+    lib.mega_moe_workspace_size.restype = ctypes.c_int
+    lib.mega_moe_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mega_moe_workspace_views.restype = ctypes.c_int
+    lib.mega_moe_workspace_views.argtypes = [P, vp, ctypes.POINTER(_Views)]
+    lib.mega_moe_forward.restype = ctypes.c_int
+    lib.mega_moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.mega_moe_forward_profiled.restype = ctypes.c_int
+    lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    if lib.mega_moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI {lib.mega_moe_abi_version()}, expected {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it cannot be loaded)."""
+    return _load()
+
+
+def mega_moe_abi_version() -> int:
+    return _load().mega_moe_abi_version()
+
+
+def mega_moe_strerror(status: int) -> str:
+    return _load().mega_moe_strerror(int(status)).decode()
+
+
+def mega_moe_workspace_size(problem: Problem) -> int:
+    out = ctypes.c_size_t(0)
+    st = _load().mega_moe_workspace_size(ctypes.byref(problem), ctypes.byref(out))
+    if st:
+        raise MegaMoEError(st, "mega_moe_workspace_size")
+    return out.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(name, t, device, dtypes, shape):
+    import torch
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def expected_shapes(problem: Problem) -> dict:
+    import torch
+    T, H, I, E, k = (problem.num_tokens, problem.hidden, problem.intermediate,
+                     problem.num_experts, problem.topk)
+    u8, f32, i32 = (torch.uint8,), (torch.float32,), (torch.int32,)
+    b16 = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
+    if problem.recipe == RECIPE_FP8_B128:
+        return dict(x=(u8, (T, H)), x_sf=(f32, (T, H // 128)), topk_idx=(i32, (T, k)), topk_w=(f32, (T, k)),
+                    l1_w=(u8, (E, 2 * I, H)), l1_sf=(f32, (E, 2 * I // 128, H // 128)),
+                    l2_w=(u8, (E, H, I)), l2_sf=(f32, (E, H // 128, I // 128)), y=(b16, (T, H)))
+    return dict(x=(u8, (T, H)), x_sf=(u8, (T, H // 32)), topk_idx=(i32, (T, k)), topk_w=(f32, (T, k)),
+                l1_w=(u8, (E, 2 * I, H // 2)), l1_sf=(u8, (E, 2 * I, H // 32)),
+                l2_w=(u8, (E, H, I // 2)), l2_sf=(u8, (E, H, I // 32)), y=(b16, (T, H)))
+
+
+NUM_PHASE_EVENTS = 5
+
+
+def mega_moe_forward(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
+                     workspace, stream=None) -> None:
+    """Enqueue the layer forward on ``stream`` (default: torch's current stream of x's device)."""
+    _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, None)
+
+
+def mega_moe_forward_profiled(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
+                              workspace, events, stream=None) -> None:
+    """mega_moe_forward that also records the given raw hipEvent_t handles (ints) at the
+    phase boundaries: before dispatch, after dispatch, after L1, after L2, after combine."""
+    _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, events)
+
+
+def _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, events):
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("mega_moe_forward needs device tensors")
+    shapes = expected_shapes(problem)
+    tensors = dict(x=x, x_sf=x_sf, topk_idx=topk_idx, topk_w=topk_w, l1_w=l1_w, l1_sf=l1_sf,
+                   l2_w=l2_w, l2_sf=l2_sf, y=y)
+    for name, t in tensors.items():
+        dts, shp = shapes[name]
+        _check_tensor(name, t, dev, dts, shp)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    nbytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    args = (ctypes.byref(problem), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_w),
+            _ptr(l1_w), _ptr(l1_sf), _ptr(l2_w), _ptr(l2_sf), _ptr(y),
+            _ptr(workspace), nbytes, ctypes.c_void_p(handle))
+    if events is None:
+        st = _load().mega_moe_forward(*args)
+        what = "mega_moe_forward"
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
+        st = _load().mega_moe_forward_profiled(*args, arr, len(events))
+        what = "mega_moe_forward_profiled"
+    if st:
+        raise MegaMoEError(st, what)
+
+
+def mega_moe_workspace_views(problem: Problem, workspace) -> dict:
+    """Torch views (on the workspace's device) of the dispatch metadata and intermediates."""
+    import torch
+    v = _Views()
+    st = _load().mega_moe_workspace_views(ctypes.byref(problem), _ptr(workspace), ctypes.byref(v))
+    if st:
+        raise MegaMoEError(st, "mega_moe_workspace_views")
+    base = workspace.data_ptr()
+    raw = workspace.view(torch.uint8).reshape(-1)
+    T, H, I, E, k = (problem.num_tokens, problem.hidden, problem.intermediate,
+                     problem.num_experts, problem.topk)
+    P = T * k
+    g = 128 if problem.recipe == RECIPE_FP8_B128 else 32
+
+    def view(addr, nbytes, dtype, shape):
+        off = addr - base
+        return raw[off:off + nbytes].view(dtype).reshape(shape)
+
+    sf_dtype = torch.float32 if problem.recipe == RECIPE_FP8_B128 else torch.uint8
+    sf_size = 4 if problem.recipe == RECIPE_FP8_B128 else 1
+    return dict(
+        expert_count=view(v.expert_count, 4 * E, torch.int32, (E,)),
+        expert_offset=view(v.expert_offset, 4 * (E + 1), torch.int32, (E + 1,)),
+        pool_src=view(v.pool_src, 4 * P, torch.int32, (P,)),
+        pair_pos=view(v.pair_pos, 4 * P, torch.int32, (P,)),
+        num_invalid=view(v.num_invalid, 4, torch.int32, (1,)),
+        inter_q=view(v.inter_q, P * I, torch.uint8, (P, I)),
+        inter_sf=view(v.inter_sf, P * (I // g) * sf_size, sf_dtype, (P, I // g)),
+        slot=view(v.slot, P * H * 2, torch.int16, (P, H)),
+    )
+
+
+class MegaMoE:
+    """Owns a workspace for repeated forwards of one problem shape on one device."""
+
+    def __init__(self, problem: Problem, device="cuda"):
+        import torch
+        self.problem = problem
+        self.device = torch.device(device)
+        self.workspace = torch.empty(max(1, mega_moe_workspace_size(problem)), dtype=torch.uint8,
+                                     device=self.device)
+
+    def __call__(self, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty(self.problem.num_tokens, self.problem.hidden, dtype=torch.bfloat16,
+                            device=self.device)
+        mega_moe_forward(self.problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
+                         self.workspace, stream)
+        return y
+
+    def views(self):
+        return mega_moe_workspace_views(self.problem, self.workspace)

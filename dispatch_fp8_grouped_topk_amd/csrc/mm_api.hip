@@ -1,0 +1,223 @@
+// C ABI of libmegamoe: argument validation, workspace carving and the launch sequence.
+// No allocation, no synchronisation: every kernel is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+#include "mega_moe.h"
+#include "mm_common.h"
+
+#define MM_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Layout {
+  size_t hdr, count, offset, blk, blk_inv, pair_pos, pool_src, w_pool, tiles_s, tiles_l, inter_q,
+      inter_sf, slot, total;
+  int P, NB, max_tiles_s, max_tiles_l;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int check_problem(const mega_moe_problem* p) {
+  if (!p) return MEGA_MOE_ERR_NULL_POINTER;
+  if (p->num_tokens < 0) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->hidden <= 0 || p->hidden % 128 || p->hidden > 16384) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->intermediate <= 0 || p->intermediate % 128 || p->intermediate > 16384) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->num_experts < 1 || p->num_experts > mm::kMaxExperts) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->topk < 1 || p->topk > mm::kMaxTopk) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->recipe != MEGA_MOE_RECIPE_FP8_B128 && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32) return MEGA_MOE_ERR_INVALID_ARG;
+  if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->flags & ~MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
+  if ((p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->num_tokens * (int64_t)p->topk > (int64_t)(INT_MAX / 2)) return MEGA_MOE_ERR_INVALID_ARG;
+  return MEGA_MOE_OK;
+}
+
+Layout make_layout(const mega_moe_problem* p) {
+  Layout L{};
+  const size_t T = (size_t)p->num_tokens, H = p->hidden, I = p->intermediate, E = p->num_experts;
+  const size_t P = T * (size_t)p->topk;
+  L.P = (int)P;
+  L.NB = (int)((P + mm::kRouteBlock - 1) / mm::kRouteBlock);
+  const size_t ts = P ? std::min(P, (P + mm::kSmallRows - 1) / mm::kSmallRows + E) : 0;
+  const size_t tl = P ? std::min(P, (P + mm::kLargeRows - 1) / mm::kLargeRows + E) : 0;
+  L.max_tiles_s = (int)ts;
+  L.max_tiles_l = (int)tl;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  L.hdr = take(mm::kHdrWords * 4);
+  L.count = take(E * 4);
+  L.offset = take((E + 1) * 4);
+  L.blk = take((size_t)L.NB * E * 4);
+  L.blk_inv = take((size_t)L.NB * 4);
+  L.pair_pos = take(P * 4);
+  L.pool_src = take(P * 4);
+  L.w_pool = take(P * 4);
+  L.tiles_s = take(ts * 8);
+  L.tiles_l = take(tl * 8);
+  L.inter_q = take(P * I);
+  L.inter_sf = take(p->recipe == MEGA_MOE_RECIPE_FP8_B128 ? P * (I / 128) * 4 : P * (I / 32));
+  L.slot = take(P * H * 2);
+  L.total = o;
+  return L;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MEGA_MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MEGA_MOE_ERR_UNSUPPORTED_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MEGA_MOE_OK : MEGA_MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+inline bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+}  // namespace
+
+MM_EXPORT int mega_moe_abi_version(void) { return MEGA_MOE_ABI_VERSION; }
+
+MM_EXPORT const char* mega_moe_strerror(int status) {
+  switch (status) {
+    case MEGA_MOE_OK: return "ok";
+    case MEGA_MOE_ERR_INVALID_ARG: return "invalid argument (a problem field is out of range)";
+    case MEGA_MOE_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MEGA_MOE_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case MEGA_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mega_moe_workspace_size()";
+    case MEGA_MOE_ERR_UNSUPPORTED_DEVICE: return "the current device is not gfx950 (MI355X)";
+    case MEGA_MOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+MM_EXPORT int mega_moe_workspace_size(const mega_moe_problem* p, size_t* bytes_out) {
+  const int st = check_problem(p);
+  if (st) return st;
+  if (!bytes_out) return MEGA_MOE_ERR_NULL_POINTER;
+  *bytes_out = make_layout(p).total;
+  return MEGA_MOE_OK;
+}
+
+MM_EXPORT int mega_moe_workspace_views(const mega_moe_problem* p, const void* workspace,
+                                       mega_moe_views* out) {
+  const int st = check_problem(p);
+  if (st) return st;
+  if (!workspace || !out) return MEGA_MOE_ERR_NULL_POINTER;
+  const Layout L = make_layout(p);
+  const uint8_t* b = static_cast<const uint8_t*>(workspace);
+  out->expert_count = reinterpret_cast<const int32_t*>(b + L.count);
+  out->expert_offset = reinterpret_cast<const int32_t*>(b + L.offset);
+  out->pool_src = reinterpret_cast<const int32_t*>(b + L.pool_src);
+  out->pair_pos = reinterpret_cast<const int32_t*>(b + L.pair_pos);
+  out->num_invalid = reinterpret_cast<const int32_t*>(b + L.hdr) + mm::kHdrInvalid;
+  out->inter_q = b + L.inter_q;
+  out->inter_sf = b + L.inter_sf;
+  out->slot = reinterpret_cast<const uint16_t*>(b + L.slot);
+  return MEGA_MOE_OK;
+}
+
+namespace {
+int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
+                 const int32_t* topk_idx, const float* topk_w, const void* l1_w,
+                 const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
+                 void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                 int num_events) {
+  int st = check_problem(p);
+  if (st) return st;
+  const Layout L = make_layout(p);
+  if (p->num_tokens == 0) return MEGA_MOE_OK;
+  const void* ptrs[] = {x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace};
+  for (const void* q : ptrs)
+    if (!q) return MEGA_MOE_ERR_NULL_POINTER;
+  for (const void* q : ptrs)
+    if (misaligned(q)) return MEGA_MOE_ERR_MISALIGNED;
+  if (workspace_bytes < L.total) return MEGA_MOE_ERR_WORKSPACE_TOO_SMALL;
+  st = check_device();
+  if (st) return st;
+
+  mm::Args a{};
+  a.x = static_cast<const uint8_t*>(x);
+  a.x_sf = x_sf;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.l1_w = static_cast<const uint8_t*>(l1_w);
+  a.l1_sf = l1_sf;
+  a.l2_w = static_cast<const uint8_t*>(l2_w);
+  a.l2_sf = l2_sf;
+  a.y = static_cast<uint16_t*>(y);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.hdr = reinterpret_cast<int32_t*>(w + L.hdr);
+  a.count = reinterpret_cast<int32_t*>(w + L.count);
+  a.offset = reinterpret_cast<int32_t*>(w + L.offset);
+  a.blk = reinterpret_cast<int32_t*>(w + L.blk);
+  a.blk_inv = reinterpret_cast<int32_t*>(w + L.blk_inv);
+  a.pair_pos = reinterpret_cast<int32_t*>(w + L.pair_pos);
+  a.pool_src = reinterpret_cast<int32_t*>(w + L.pool_src);
+  a.w_pool = reinterpret_cast<float*>(w + L.w_pool);
+  a.tiles_s = reinterpret_cast<int2*>(w + L.tiles_s);
+  a.tiles_l = reinterpret_cast<int2*>(w + L.tiles_l);
+  a.inter_q = w + L.inter_q;
+  a.inter_sf = w + L.inter_sf;
+  a.slot = reinterpret_cast<uint16_t*>(w + L.slot);
+  a.T = (int)p->num_tokens;
+  a.H = p->hidden;
+  a.I = p->intermediate;
+  a.E = p->num_experts;
+  a.k = p->topk;
+  a.P = L.P;
+  a.NB = L.NB;
+  a.recipe = p->recipe;
+  a.clamp = std::isinf(p->swiglu_clamp) ? 0.f : p->swiglu_clamp;
+  a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
+  a.large_min_rows = INT_MAX;          // the large-M tile class is not enabled yet
+  if (a.tile_mode == MEGA_MOE_FLAG_TILE_LARGE) a.tile_mode = MEGA_MOE_FLAG_TILE_SMALL;
+  a.max_tiles_s = L.max_tiles_s;
+  a.max_tiles_l = L.max_tiles_l;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> bool {
+    return i >= num_events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return MEGA_MOE_ERR_HIP;
+  if (mm::launch_route(a, s) != hipSuccess || !mark(1)) return MEGA_MOE_ERR_HIP;
+  if (mm::launch_l1_small(a, s) != hipSuccess || !mark(2)) return MEGA_MOE_ERR_HIP;
+  if (mm::launch_l2_small(a, s) != hipSuccess || !mark(3)) return MEGA_MOE_ERR_HIP;
+  if (mm::launch_combine(a, s) != hipSuccess || !mark(4)) return MEGA_MOE_ERR_HIP;
+  return MEGA_MOE_OK;
+}
+}  // namespace
+
+MM_EXPORT int mega_moe_forward(const mega_moe_problem* p, const void* x, const void* x_sf,
+                               const int32_t* topk_idx, const float* topk_w, const void* l1_w,
+                               const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
+                      workspace_bytes, stream, nullptr, 0);
+}
+
+MM_EXPORT int mega_moe_forward_profiled(const mega_moe_problem* p, const void* x, const void* x_sf,
+                                        const int32_t* topk_idx, const float* topk_w,
+                                        const void* l1_w, const void* l1_sf, const void* l2_w,
+                                        const void* l2_sf, void* y, void* workspace,
+                                        size_t workspace_bytes, void* stream, void* const* events,
+                                        int num_events) {
+  if (num_events < 0 || num_events > MEGA_MOE_NUM_PHASE_EVENTS || (num_events > 0 && !events))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < num_events; ++i)
+    if (!events[i]) return MEGA_MOE_ERR_NULL_POINTER;
+  return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
+                      workspace_bytes, stream, events, num_events);
+}

@@ -1,0 +1,147 @@
+// Internal definitions shared by the HIP translation units of libmegamoe.
+// gfx950 (CDNA4) only: 64-wide wavefronts, FP8/FP4 MFMA with E8M0 block scales.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+// ------------------------------------------------------------------------------------------
+// Limits and tile geometry
+constexpr int kMaxExperts = 8192;     // LDS arrays of the scan kernel hold one int per expert
+constexpr int kMaxTopk = 64;
+constexpr int kRouteBlock = 256;      // pairs per dispatch workgroup
+constexpr int kSmallRows = 64;        // pool rows per small-M tile (4 MFMA column groups of 16)
+constexpr int kLargeRows = 128;       // pool rows per large-M tile
+constexpr int kL1SlabCh = 128;        // intermediate channels per L1 workgroup (gate+up = 256 rows)
+constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgroup
+constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Workspace header words.
+enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrWords = 64 };
+
+struct Args {
+  // inputs
+  const uint8_t* x;
+  const void* x_sf;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const uint8_t* l1_w;
+  const void* l1_sf;
+  const uint8_t* l2_w;
+  const void* l2_sf;
+  uint16_t* y;
+  // workspace regions
+  int32_t* hdr;
+  int32_t* count;       // [E]
+  int32_t* offset;      // [E+1]
+  int32_t* blk;         // [NB][E] per-dispatch-block counts, then bases
+  int32_t* blk_inv;     // [NB]
+  int32_t* pair_pos;    // [P]
+  int32_t* pool_src;    // [P]
+  float* w_pool;        // [P]
+  int2* tiles_s;        // small-M tile list {expert, first pool row}
+  int2* tiles_l;        // large-M tile list
+  uint8_t* inter_q;     // [P, I]
+  void* inter_sf;       // [P, I/128] f32 | [P, I/32] u8
+  uint16_t* slot;       // [P, H] bf16, row = pair
+  // sizes
+  int T, H, I, E, k, P, NB;
+  int recipe;
+  float clamp;          // <= 0: none
+  int tile_mode;        // 0 auto, 1 small only, 2 large only
+  int large_min_rows;   // auto mode: experts with at least this many rows use the large class
+  int max_tiles_s, max_tiles_l;
+};
+
+// ------------------------------------------------------------------------------------------
+// Numeric helpers (device)
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// Four floats -> four OCP E4M3FN bytes (element 0 in the low byte), round to nearest even.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// UE8M0 code of the smallest power of two 2^E with amax / 2^E <= 448:
+// r = amax / 448 (IEEE division), E = ceil(log2 r) read off r's exponent and mantissa bits,
+// code = clamp(E + 127, 0, 254); amax == 0 -> 0.
+__device__ __forceinline__ uint32_t ue8m0_for_amax(float amax) {
+  float r = amax / 448.0f;
+  uint32_t u = __float_as_uint(r);
+  uint32_t ex = (u >> 23) & 0xFFu;
+  uint32_t man = u & 0x7FFFFFu;
+  if (ex == 0) return 0u;                     // r subnormal or zero: E <= -127
+  uint32_t code = man ? ex + 1 : ex;          // code = E + 127
+  return code > 254u ? 254u : code;
+}
+
+// 16x16x128 FP8 x FP8 MFMA with unit block scales: D = A * B (C = 0).
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x128 E2M1 (A) x E4M3 (B) MFMA with per-32-K E8M0 scales, accumulating into c.
+__device__ __forceinline__ v4f mfma_fp4w_fp8(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+}
+
+// E4M3 (A) x E4M3 (B) with E8M0 scales, accumulating into c.
+__device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// MFMA 16x16x128 operand layout on gfx950 (measured):
+//  * FP8: lane l carries row (l % 16); its bytes 0..15 are K [16*(l/16), +16) and its
+//    bytes 16..31 are K [64 + 16*(l/16), +16) of the 128-wide K block.
+//  * FP4: lane l carries row (l % 16), K [32*(l/16), +32) as 16 bytes, low nibble first.
+//  * E8M0 scales: the scale of (row m, 32-wide K group g) is read from lane m + 16*g.
+//  * D (16x16 f32): lane l holds column (l % 16), rows 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row_kblock, int lg) {
+  v4i lo = *reinterpret_cast<const v4i*>(row_kblock + 16 * lg);
+  v4i hi = *reinterpret_cast<const v4i*>(row_kblock + 64 + 16 * lg);
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ v8i load_fp4_operand(const uint8_t* row_kblock_packed, int lg) {
+  v4i lo = *reinterpret_cast<const v4i*>(row_kblock_packed + 16 * lg);
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+// XCD-aware workgroup order: the hardware deals workgroup ids round-robin over the 8 XCDs;
+// this returns a logical id such that each XCD walks one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_logical_id(int hw_id, int grid) {
+  int per = grid >> 3;                 // grid is a multiple of 8
+  return (hw_id & 7) * per + (hw_id >> 3);
+}
+
+}  // namespace mm
+
+// Host launchers (one per translation unit).
+namespace mm {
+hipError_t launch_route(const Args& a, hipStream_t s);
+hipError_t launch_l1_small(const Args& a, hipStream_t s);
+hipError_t launch_l2_small(const Args& a, hipStream_t s);
+hipError_t launch_combine(const Args& a, hipStream_t s);
+}  // namespace mm

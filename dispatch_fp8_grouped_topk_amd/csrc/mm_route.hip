@@ -1,0 +1,206 @@
+// Dispatch (per-expert histogram, prefix scan, stable scatter + tile lists) and combine.
+//
+// Dispatch follows the MegaMoE dispatch role (research report "MegaMoE on SM100/SM90",
+// section 3.1; design page "MegaMoE SM90 Implementation Design", section 9.2): count the
+// rows each expert receives, lay the experts' pools out back to back and record, per pool
+// row, its source {token, top-k slot}.  The pages fill pools with racing atomics; here a
+// pool keeps row-major (token, slot) order so the result is unique and repeatable: a pair's
+// rank is (pairs of the same expert in earlier dispatch blocks) + (earlier pairs of the same
+// expert inside its block), both computed from positions, never from atomic return order.
+//
+// Combine follows the design page's combine reduce (section 11.2): for each token, sum its
+// active top-k BF16 rows in float32 in ascending slot order and store BF16.
+#include "mm_common.h"
+
+namespace mm {
+
+// ---------------------------------------------------------------------------------- count
+// One workgroup per 256 consecutive pairs: LDS histogram of expert ids (written out as the
+// block's row of blk[NB][E]) and each pair's rank among same-expert pairs of the block.
+__global__ __launch_bounds__(kRouteBlock) void k_route_count(Args a) {
+  extern __shared__ int hist[];             // [E]
+  __shared__ int ids[kRouteBlock];
+  __shared__ int inv_w[kRouteBlock / 64];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int pair = b * kRouteBlock + tid;
+  for (int i = tid; i < a.E; i += kRouteBlock) hist[i] = 0;
+  int e = pair < a.P ? a.topk_idx[pair] : -1;
+  const bool valid = e >= 0 && e < a.E;
+  const bool invalid = pair < a.P && e >= a.E;
+  ids[tid] = valid ? e : -1;
+  __syncthreads();
+  int rank = 0;
+  if (valid) {
+    for (int t = 0; t < tid; ++t) rank += (ids[t] == e);
+    atomicAdd(&hist[e], 1);
+  }
+  unsigned long long inv = __ballot(invalid);
+  if ((tid & 63) == 0) inv_w[tid >> 6] = __popcll(inv);
+  __syncthreads();
+  for (int i = tid; i < a.E; i += kRouteBlock) a.blk[(size_t)b * a.E + i] = hist[i];
+  if (pair < a.P) a.pair_pos[pair] = valid ? rank : -1;
+  if (tid == 0) {
+    int s = 0;
+    for (int w = 0; w < kRouteBlock / 64; ++w) s += inv_w[w];
+    a.blk_inv[b] = s;
+  }
+}
+
+// Inclusive scan of one int per thread over a 1024-thread workgroup; returns the inclusive
+// value and writes the workgroup total to *total.
+__device__ int block_scan_1024(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  // wave-level inclusive scan
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < 16 ? sh[lane] : 0;
+    for (int d = 1; d < 16; d <<= 1) {
+      int o = __shfl_up(s, d, 64);
+      if (lane >= d) s += o;
+    }
+    if (lane < 16) sh[16 + lane] = s;
+  }
+  __syncthreads();
+  int base = w > 0 ? sh[16 + w - 1] : 0;
+  *total = sh[16 + 15];
+  __syncthreads();
+  return v + base;
+}
+
+// ---------------------------------------------------------------------------------- scan
+// One workgroup of 1024 threads: per-expert totals and per-block bases (in place in blk),
+// expert offsets, the invalid-id total and the tile lists of both GEMM tile classes.
+__global__ __launch_bounds__(1024) void k_route_scan(Args a) {
+  __shared__ int s_count[kMaxExperts];
+  __shared__ int part[4][256];
+  __shared__ int sh[64];
+  const int tid = threadIdx.x;
+  const int E = a.E, NB = a.NB;
+
+  // 1. totals and block bases; threads (el, q): expert e0+el, quarter q of the blocks
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int el = tid & 255, q = tid >> 8;
+    const int e = e0 + el;
+    const int b_lo = (q * NB) >> 2, b_hi = ((q + 1) * NB) >> 2;
+    int s = 0;
+    if (e < E) {
+#pragma unroll 8
+      for (int b = b_lo; b < b_hi; ++b) s += a.blk[(size_t)b * E + e];
+    }
+    part[q][el] = s;
+    __syncthreads();
+    if (e < E) {
+      int run = 0;
+      for (int qq = 0; qq < q; ++qq) run += part[qq][el];
+      for (int b = b_lo; b < b_hi; ++b) {
+        const int c = a.blk[(size_t)b * E + e];
+        a.blk[(size_t)b * E + e] = run;
+        run += c;
+      }
+      if (q == 3) s_count[e] = run;
+    }
+    __syncthreads();
+  }
+
+  // 2. offsets (exclusive scan of counts) and the tile lists
+  int carry = 0, carry_s = 0, carry_l = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + tid;
+    const int c = e < E ? s_count[e] : 0;
+    bool large;
+    if (a.tile_mode == 1) large = false;
+    else if (a.tile_mode == 2) large = true;
+    else large = c >= a.large_min_rows;
+    const int nts = large ? 0 : (c + kSmallRows - 1) / kSmallRows;
+    const int ntl = large ? (c + kLargeRows - 1) / kLargeRows : 0;
+    int tot, tot_s, tot_l;
+    const int inc = block_scan_1024(c, sh, &tot);
+    const int inc_s = block_scan_1024(nts, sh, &tot_s);
+    const int inc_l = block_scan_1024(ntl, sh, &tot_l);
+    if (e < E) {
+      a.count[e] = c;
+      a.offset[e] = carry + inc - c;
+      const int bs = carry_s + inc_s - nts;
+      for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);
+      const int bl = carry_l + inc_l - ntl;
+      for (int i = 0; i < ntl; ++i) a.tiles_l[bl + i] = make_int2(e, i * kLargeRows);
+    }
+    carry += tot;
+    carry_s += tot_s;
+    carry_l += tot_l;
+  }
+  if (tid == 0) {
+    a.offset[E] = carry;
+    a.hdr[kHdrTilesSmall] = carry_s;
+    a.hdr[kHdrTilesLarge] = carry_l;
+    int inv = 0;
+    for (int b = 0; b < NB; ++b) inv += a.blk_inv[b];
+    a.hdr[kHdrInvalid] = inv;
+  }
+}
+
+// ---------------------------------------------------------------------------------- scatter
+__global__ __launch_bounds__(kRouteBlock) void k_route_scatter(Args a) {
+  const int b = blockIdx.x;
+  const int pair = b * kRouteBlock + threadIdx.x;
+  if (pair >= a.P) return;
+  const int r = a.pair_pos[pair];
+  if (r < 0) return;
+  const int e = a.topk_idx[pair];
+  const int pos = a.offset[e] + a.blk[(size_t)b * a.E + e] + r;
+  a.pair_pos[pair] = pos;
+  a.pool_src[pos] = pair;
+  a.w_pool[pos] = a.topk_w[pair];
+}
+
+hipError_t launch_route(const Args& a, hipStream_t s) {
+  if (a.P == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_count, dim3(a.NB), dim3(kRouteBlock), (size_t)a.E * sizeof(int), s, a);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_route_scatter, dim3(a.NB), dim3(kRouteBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------- combine
+// grid (ceil(H / 2048), min(T, 65535)); each thread owns 8 consecutive columns of a token
+// and strides over tokens.
+__global__ __launch_bounds__(256) void k_combine(Args a) {
+  const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (n0 >= a.H) return;
+  for (int t = blockIdx.y; t < a.T; t += gridDim.y) {
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const int pair = t * a.k + j;
+    if (a.pair_pos[pair] < 0) continue;          // masked or invalid slot
+    const v4i v = *reinterpret_cast<const v4i*>(a.slot + (size_t)pair * a.H + n0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = (uint32_t)v[i];
+      acc[2 * i] += __uint_as_float(w << 16);
+      acc[2 * i + 1] += __uint_as_float(w & 0xFFFF0000u);
+    }
+  }
+  v4i o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (int)(bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16));
+  *reinterpret_cast<v4i*>(a.y + (size_t)t * a.H + n0) = o;
+  }
+}
+
+hipError_t launch_combine(const Args& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  dim3 grid((a.H + 2047) / 2048, a.T < 65535 ? a.T : 65535);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mm

@@ -1,0 +1,156 @@
+/*
+ * mega_moe.h -- C ABI of the MegaMoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, on one GPU, the forward of a mixture-of-experts FFN layer:
+ *
+ *   1. dispatch   every (token t, top-k slot j) pair with expert id e in [0, E)
+ *                 joins expert e's pool; rows of a pool keep row-major (t, j) order.
+ *                 (Research report "MegaMoE on SM100/SM90", section 3.1, dispatch
+ *                 role; design page "MegaMoE SM90 Implementation Design",
+ *                 section 9.2, source metadata {rank, token, topk}.)
+ *   2. L1 GEMM    acc = sum_kb sx[t,kb] * sw1[e,n,kb] * sum_{k in kb} x[t,k] w1[e,n,k]
+ *                 over n in [0, 2I)  (design page section 5.3, scale application;
+ *                 section 15.2, weight-scale layout).
+ *   3. SwiGLU     v = clamp(silu(acc[:, :I]) * acc[:, I:]) * topk_w[t, j]
+ *                 then per group of G channels: float scale amax/448 (G = 128) or
+ *                 UE8M0 scale (G = 32) and an E4M3 cast  (design page section 10.1).
+ *   4. L2 GEMM    o = the same block-scaled product of the re-quantised
+ *                 intermediate with w2, cast to BF16 per (token, slot) row
+ *                 (design page section 11.1).
+ *   5. combine    y[t] = bf16( sum_j f32(slot row (t, j)) ), ascending j, float32
+ *                 accumulation (design page section 11.2).
+ *
+ * Recipes:
+ *   MEGA_MOE_RECIPE_FP8_B128   x, w1, w2 and the intermediate are OCP E4M3FN bytes;
+ *                              float32 scales: x per (token, 128 channels), weights
+ *                              per 128x128 block, intermediate per (row, 128 channels).
+ *                              (The SM90 FP8 path of the design page, section 1.1.)
+ *   MEGA_MOE_RECIPE_MXFP4W_B32 x and the intermediate are E4M3FN with a UE8M0 scale per
+ *                              32 channels; w1, w2 are E2M1 nibbles (two per byte, low
+ *                              nibble = even K index) with a UE8M0 scale per (row, 32 K).
+ *                              (PR #411 "SM90 FP8 x MXFP4 MegaMoE"; UE8M0 = 2^(code-127).)
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   x        u8  [T, H]                     x_sf  f32 [T, H/128]  | u8 [T, H/32]
+ *   topk_idx i32 [T, k]                     topk_w f32 [T, k]
+ *   l1_w     u8  [E, 2I, H]  | [E, 2I, H/2] rows 0..I-1 gate, I..2I-1 up
+ *   l1_sf    f32 [E, 2I/128, H/128]         | u8 [E, 2I, H/32]
+ *   l2_w     u8  [E, H, I]   | [E, H, I/2]
+ *   l2_sf    f32 [E, H/128, I/128]          | u8 [E, H, I/32]
+ *   y        bf16 (u16 bits) [T, H]
+ * Every pointer must be 16-byte aligned.  Ids < 0 in topk_idx mark masked slots; ids
+ * >= E are dropped (contribute nothing) and counted in the num_invalid view.
+ *
+ * Ownership: the caller allocates every buffer, including the workspace.  The library
+ * allocates, frees and synchronises nothing; all work is enqueued on `stream` and the
+ * call returns at once.  Inputs are read only; y is fully overwritten.  The workspace
+ * needs no initialisation (each call re-initialises what it uses) and stays readable
+ * through mega_moe_workspace_views() until the next call that uses it.  Concurrent
+ * calls need distinct workspaces.
+ *
+ * Errors: the functions validate their arguments synchronously and return 0 or one of
+ * the negative MEGA_MOE_ERR_* codes.  Nothing is enqueued when validation fails; after
+ * MEGA_MOE_ERR_HIP (a failed launch) part of the sequence may have been enqueued and y is
+ * undefined.  T * k must stay below 2^30.
+ */
+#ifndef MEGA_MOE_H
+#define MEGA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEGA_MOE_ABI_VERSION 1
+
+typedef enum {
+  MEGA_MOE_RECIPE_FP8_B128 = 0,
+  MEGA_MOE_RECIPE_MXFP4W_B32 = 1
+} mega_moe_recipe;
+
+/* flags: bits 0-1 force the GEMM tile class (0 = choose per expert from its row
+   count, 1 = small-M class only, 2 = large-M class only); other bits must be 0. */
+#define MEGA_MOE_FLAG_TILE_AUTO  0u
+#define MEGA_MOE_FLAG_TILE_SMALL 1u
+#define MEGA_MOE_FLAG_TILE_LARGE 2u
+#define MEGA_MOE_FLAG_TILE_MASK  3u
+
+enum {
+  MEGA_MOE_OK = 0,
+  MEGA_MOE_ERR_INVALID_ARG = -1,        /* a field out of range or not a multiple of 128 */
+  MEGA_MOE_ERR_NULL_POINTER = -2,       /* a required pointer is NULL */
+  MEGA_MOE_ERR_MISALIGNED = -3,         /* a pointer is not 16-byte aligned */
+  MEGA_MOE_ERR_WORKSPACE_TOO_SMALL = -4,/* workspace_bytes < mega_moe_workspace_size() */
+  MEGA_MOE_ERR_UNSUPPORTED_DEVICE = -5, /* the current device is not gfx950 */
+  MEGA_MOE_ERR_HIP = -6                 /* a HIP runtime call or launch failed */
+};
+
+typedef struct {
+  int64_t num_tokens;    /* T >= 0; T == 0 is a valid no-op */
+  int32_t hidden;        /* H in (0, 16384], multiple of 128 */
+  int32_t intermediate;  /* I in (0, 16384], multiple of 128 */
+  int32_t num_experts;   /* E in [1, 8192]; an always-on shared expert is one more expert */
+  int32_t topk;          /* k in [1, 64] columns of topk_idx / topk_w */
+  int32_t recipe;        /* mega_moe_recipe */
+  float swiglu_clamp;    /* 0 or +inf: no clamp; c > 0: silu(g)*u clamped to [-c, c]
+                            before the top-k weight multiplies it */
+  uint32_t flags;        /* MEGA_MOE_FLAG_* */
+} mega_moe_problem;
+
+/* Device pointers into a workspace after a forward call (for inspection and tests). */
+typedef struct {
+  const int32_t* expert_count;   /* [E]   rows per expert */
+  const int32_t* expert_offset;  /* [E+1] exclusive prefix of expert_count */
+  const int32_t* pool_src;       /* [T*k] pool row -> pair t*k+j (first offset[E] valid) */
+  const int32_t* pair_pos;       /* [T*k] pair -> pool row, -1 when masked or invalid */
+  const int32_t* num_invalid;    /* [1]   ids >= E seen in topk_idx */
+  const uint8_t* inter_q;        /* [T*k, I] E4M3 intermediate per pool row */
+  const void* inter_sf;          /* [T*k, I/128] f32 | [T*k, I/32] u8 */
+  const uint16_t* slot;          /* [T*k, H] BF16 L2 output per pair (t*k+j order) */
+} mega_moe_views;
+
+/* Bytes of workspace a forward call of this problem needs (alignment 256). */
+int mega_moe_workspace_size(const mega_moe_problem* p, size_t* bytes_out);
+
+/* The layer forward; see the top of this file for the arithmetic and the layouts.
+   stream: a hipStream_t, NULL for the default stream. */
+int mega_moe_forward(const mega_moe_problem* p,
+                     const void* x, const void* x_sf,
+                     const int32_t* topk_idx, const float* topk_w,
+                     const void* l1_w, const void* l1_sf,
+                     const void* l2_w, const void* l2_sf,
+                     void* y, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* mega_moe_forward, additionally recording caller-created hipEvent_t handles on `stream` at
+   the phase boundaries, for timing each kernel of the layer on the stream it runs on:
+     events[0] before dispatch, [1] after dispatch (before L1), [2] after the L1 GEMM,
+     [3] after the L2 GEMM, [4] after the combine.
+   num_events in [0, MEGA_MOE_NUM_PHASE_EVENTS]; events beyond num_events are not recorded.
+   The caller owns the events.  With T == 0 nothing is recorded. */
+#define MEGA_MOE_NUM_PHASE_EVENTS 5
+int mega_moe_forward_profiled(const mega_moe_problem* p,
+                              const void* x, const void* x_sf,
+                              const int32_t* topk_idx, const float* topk_w,
+                              const void* l1_w, const void* l1_sf,
+                              const void* l2_w, const void* l2_sf,
+                              void* y, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int num_events);
+
+/* Fill *out with device pointers into `workspace` for problem p. */
+int mega_moe_workspace_views(const mega_moe_problem* p, const void* workspace,
+                             mega_moe_views* out);
+
+/* Static text for a status code. */
+const char* mega_moe_strerror(int status);
+
+/* MEGA_MOE_ABI_VERSION of the loaded library. */
+int mega_moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEGA_MOE_H */

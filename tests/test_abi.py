@@ -1,0 +1,94 @@
+"""The C ABI library on the CPU: it loads, exports every function include/mega_moe.h declares,
+sizes workspaces and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dispatch_fp8_grouped_topk_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(mega_moe_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = mm.library()
+    declared = _declared_functions()
+    assert {"mega_moe_forward", "mega_moe_workspace_size", "mega_moe_workspace_views",
+            "mega_moe_strerror", "mega_moe_abi_version"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strerror():
+    assert mm.mega_moe_abi_version() == mm.ABI_VERSION
+    assert mm.mega_moe_strerror(0) == "ok"
+    for st in range(-6, 0):
+        assert mm.mega_moe_strerror(st) != "unknown status"
+
+
+def _p(**kw):
+    base = dict(T=128, H=7168, I=2048, E=256, k=8)
+    base.update(kw)
+    return mm.Problem.make(base["T"], base["H"], base["I"], base["E"], base["k"],
+                           base.get("recipe", 0), base.get("clamp", 0.0), base.get("flags", 0))
+
+
+def test_workspace_size_grows_with_tokens_and_covers_buffers():
+    s1 = mm.mega_moe_workspace_size(_p(T=128))
+    s2 = mm.mega_moe_workspace_size(_p(T=8192))
+    assert s2 > s1
+    P = 8192 * 8
+    # at least the BF16 slot rows, the FP8 intermediate and its scales
+    assert s2 >= P * 7168 * 2 + P * 2048 + P * 16 * 4
+    s4 = mm.mega_moe_workspace_size(_p(T=4096, E=257, k=9, recipe=1))
+    assert s4 >= 4096 * 9 * (7168 * 2 + 2048 + 2048 // 32)
+    assert mm.mega_moe_workspace_size(_p(T=0)) > 0
+
+
+@pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
+                                dict(k=65), dict(recipe=2), dict(clamp=-1.0), dict(clamp=float("nan")),
+                                dict(flags=4), dict(flags=3), dict(T=-1), dict(H=32768)])
+def test_invalid_problem_rejected(kw):
+    with pytest.raises(mm.MegaMoEError) as ei:
+        mm.mega_moe_workspace_size(_p(**kw))
+    assert ei.value.status == -1
+
+
+def _forward_raw(problem, ptrs, ws_bytes):
+    lib = mm.library()
+    args = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return lib.mega_moe_forward(ctypes.byref(problem), *args[:9], args[9], ws_bytes, None)
+
+
+def test_forward_argument_errors_without_a_device():
+    p = _p(T=4, H=256, I=128, E=4, k=2)
+    need = mm.mega_moe_workspace_size(p)
+    good = [0x10000 * (i + 1) for i in range(10)]
+    assert _forward_raw(p, [None] + good[1:], need) == -2          # NULL x
+    bad = list(good)
+    bad[3] += 4
+    assert _forward_raw(p, bad, need) == -3                        # misaligned topk_w
+    assert _forward_raw(p, good, need - 1) == -4                   # workspace too small
+    p0 = _p(T=0, H=256, I=128, E=4, k=2)
+    assert _forward_raw(p0, [None] * 10, 0) == 0                   # T == 0: no-op
+    pbad = _p(T=4, H=200, I=128, E=4, k=2)
+    assert _forward_raw(pbad, good, need) == -1
+
+
+def test_views_null_workspace_rejected():
+    v = mm._Views()
+    lib = mm.library()
+    p = _p(T=4, H=256, I=128, E=4, k=2)
+    assert lib.mega_moe_workspace_views(ctypes.byref(p), None, ctypes.byref(v)) == -2

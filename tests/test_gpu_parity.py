@@ -1,0 +1,165 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle, on an MI355X.
+
+Small problems are compared in full (every output element, every dispatch field, every
+intermediate code); the benchmark-size workloads are compared on sampled tokens, with the
+dispatch metadata still checked in full.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import (assert_dispatch_exact, assert_intermediate_close, assert_y_close, run_gpu,
+                     run_oracle, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _custom(spec, idx=None, w=None):
+    P = synth.make_problem(spec)
+    if idx is not None:
+        P["topk_idx"] = torch.as_tensor(idx, dtype=torch.int32).contiguous()
+    if w is not None:
+        P["topk_w"] = torch.as_tensor(w, dtype=torch.float32).contiguous()
+    return P
+
+
+def _full_check(spec, P, flags=0):
+    _say(f"spec={spec} flags={flags}")
+    D = to_device(P)
+    y, views, _ = run_gpu(spec, D, flags)
+    ref = run_oracle(spec, P)
+    assert_dispatch_exact(spec, P["topk_idx"].numpy(), views)
+    assert_intermediate_close(spec, views, ref)
+    return assert_y_close(y.cpu().numpy(), ref["y"], str(spec))
+
+
+SMALL = {
+    "tiny_c0": synth.CONFIGS[0],
+    "ragged": synth.Spec(37, 640, 384, 12, 3, seed=101, weight_set=101),
+    "multi_tile": synth.Spec(300, 512, 256, 4, 2, seed=102, weight_set=102),
+    "clamp": synth.Spec(64, 512, 256, 8, 4, routing="biased", swiglu_clamp=0.05, seed=103, weight_set=103),
+    "zipf": synth.Spec(512, 512, 384, 32, 4, routing="zipf", seed=104, weight_set=104),
+    "T1": synth.Spec(1, 512, 256, 8, 2, seed=105, weight_set=105),
+    "E1_k1": synth.Spec(70, 384, 256, 1, 1, seed=106, weight_set=106),
+    "mxfp4": synth.Spec(40, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=107, weight_set=107),
+    "mxfp4_multi_tile": synth.Spec(200, 512, 256, 3, 2, recipe=1, seed=108, weight_set=108),
+    "mxfp4_clamp": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.05, seed=109, weight_set=109),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_problem_full_parity(name):
+    spec = SMALL[name]
+    _full_check(spec, synth.make_problem(spec))
+
+
+def test_all_tokens_on_one_expert():
+    spec = synth.Spec(150, 512, 256, 8, 1, seed=110, weight_set=110)
+    _full_check(spec, _custom(spec, idx=np.full((150, 1), 5)))
+
+
+def test_masked_and_invalid_ids():
+    spec = synth.Spec(33, 512, 256, 6, 3, seed=111, weight_set=111)
+    P = synth.make_problem(spec)
+    idx = P["topk_idx"].numpy().copy()
+    rng = np.random.default_rng(0)
+    idx[rng.random(idx.shape) < 0.2] = -1
+    idx[rng.random(idx.shape) < 0.1] = 6 + 3
+    _full_check(spec, _custom(spec, idx=idx))
+
+
+def test_empty_experts_and_skew():
+    spec = synth.Spec(90, 512, 256, 16, 2, seed=112, weight_set=112)
+    rng = np.random.default_rng(1)
+    idx = np.stack([rng.choice([0, 3, 15], 90), rng.choice([1, 4], 90)], axis=1)
+    _full_check(spec, _custom(spec, idx=idx))
+
+
+def test_zero_tokens_is_a_noop():
+    spec = synth.Spec(0, 512, 256, 8, 2)
+    D = to_device(synth.make_problem(spec))
+    y, views, _ = run_gpu(spec, D)
+    assert y.shape == (0, 512)
+
+
+def test_repeatable_and_stale_workspace():
+    spec = SMALL["zipf"]
+    _say(f"repeatability {spec}")
+    D = to_device(synth.make_problem(spec))
+    y1, _, ws = run_gpu(spec, D)
+    y2, _, _ = run_gpu(spec, D, workspace=ws)
+    y3, _, _ = run_gpu(spec, D, workspace=ws, fill=0xFF)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+@pytest.mark.parametrize("recipe", [0, 1])
+def test_power_of_two_topk_weight_scaling_is_bitwise(recipe):
+    spec = synth.Spec(64, 512, 256, 8, 3, recipe=recipe, seed=113, weight_set=113)
+    _say(f"pow2 scaling {spec}")
+    D = to_device(synth.make_problem(spec))
+    y1, _, _ = run_gpu(spec, D)
+    D2 = dict(D)
+    D2["topk_w"] = D["topk_w"] * 0.25
+    y2, _, _ = run_gpu(spec, D2)
+    assert torch.equal(y1.view(torch.bfloat16).float() * 0.25, y2.view(torch.bfloat16).float())
+
+
+def test_one_hot_weights_equal_selected_slot():
+    spec = synth.Spec(40, 512, 256, 8, 3, seed=114, weight_set=114)
+    P = synth.make_problem(spec)
+    w = torch.zeros(40, 3)
+    w[:, 2] = 1.0
+    P["topk_w"] = w
+    D = to_device(P)
+    y, views, _ = run_gpu(spec, D)
+    slot = views["slot"].view(40, 3, 512)[:, 2]
+    assert torch.equal(y, slot)
+
+
+# ------------------------------------------------------------------------------ benchmark sizes
+_DEV_CACHE = {}
+
+
+def _device_problem(cfg):
+    """Benchmark-size inputs generated on the GPU (weights shared between configs 1 and 3)."""
+    spec = synth.CONFIGS[cfg]
+    key = (spec.weight_set, spec.H, spec.I, spec.E, spec.recipe)
+    if key not in _DEV_CACHE:
+        _DEV_CACHE.clear()
+        torch.cuda.empty_cache()
+        _DEV_CACHE[key] = synth.make_weights(spec, "cuda")
+    P = dict(_DEV_CACHE[key])
+    idx, w = synth.make_routing(spec)
+    x, x_sf = synth.make_activations(spec, "cuda")
+    P.update(x=x, x_sf=x_sf, topk_idx=idx.cuda(), topk_w=w.cuda())
+    return spec, P
+
+
+def _sample_tokens(spec, idx, n=3):
+    counts = np.bincount(idx[idx >= 0].reshape(-1), minlength=spec.E)
+    hot = int(np.argmax(counts))
+    last_hot = int(np.nonzero((idx == hot).any(axis=1))[0][-1])     # deepest row of the hottest pool
+    toks = [0, spec.T - 1, last_hot][:n]
+    return sorted(set(toks))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_benchmark_config_sampled_parity(cfg):
+    spec, P = _device_problem(cfg)
+    _say(f"config {cfg}: {spec.name}")
+    y, views, _ = run_gpu(spec, P)
+    idx = P["topk_idx"].cpu().numpy()
+    assert_dispatch_exact(spec, idx, views)
+    toks = _sample_tokens(spec, idx)
+    ref = run_oracle(spec, P, tokens=toks)
+    assert_intermediate_close(spec, views, ref)
+    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
+    _say(f"config {cfg}: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")

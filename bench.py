@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
-    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the CPU-oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
     args = ap.parse_args()

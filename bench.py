@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the timed region, run one elementwise float32 copy of this many MiB "
+                         "(reads and writes exactly that many bytes) to calibrate HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -156,6 +159,15 @@ def main():
     y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], P["l1_sf"], P["l2_w"], P["l2_sf"], y, ws)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)            # one kernel: reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         mm.mega_moe_forward(*call, stream=stream)

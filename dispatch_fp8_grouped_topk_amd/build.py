@@ -23,6 +23,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the FP8 recipe promotes every MFMA result with VALU FMAs,
+    # which cannot read AGPRs directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]

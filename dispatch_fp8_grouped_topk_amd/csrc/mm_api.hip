@@ -182,8 +182,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.recipe = p->recipe;
   a.clamp = std::isinf(p->swiglu_clamp) ? 0.f : p->swiglu_clamp;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
-  a.large_min_rows = INT_MAX;          // the large-M tile class is not enabled yet
-  if (a.tile_mode == MEGA_MOE_FLAG_TILE_LARGE) a.tile_mode = MEGA_MOE_FLAG_TILE_SMALL;
+  a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;
   a.max_tiles_l = L.max_tiles_l;
 
@@ -193,8 +192,10 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   };
   if (!mark(0)) return MEGA_MOE_ERR_HIP;
   if (mm::launch_route(a, s) != hipSuccess || !mark(1)) return MEGA_MOE_ERR_HIP;
-  if (mm::launch_l1_small(a, s) != hipSuccess || !mark(2)) return MEGA_MOE_ERR_HIP;
-  if (mm::launch_l2_small(a, s) != hipSuccess || !mark(3)) return MEGA_MOE_ERR_HIP;
+  if (mm::launch_l1_small(a, s) != hipSuccess || mm::launch_l1_large(a, s) != hipSuccess || !mark(2))
+    return MEGA_MOE_ERR_HIP;
+  if (mm::launch_l2_small(a, s) != hipSuccess || mm::launch_l2_large(a, s) != hipSuccess || !mark(3))
+    return MEGA_MOE_ERR_HIP;
   if (mm::launch_combine(a, s) != hipSuccess || !mark(4)) return MEGA_MOE_ERR_HIP;
   return MEGA_MOE_OK;
 }

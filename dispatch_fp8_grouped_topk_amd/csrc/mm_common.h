@@ -14,6 +14,7 @@ constexpr int kMaxTopk = 64;
 constexpr int kRouteBlock = 256;      // pairs per dispatch workgroup
 constexpr int kSmallRows = 64;        // pool rows per small-M tile (4 MFMA column groups of 16)
 constexpr int kLargeRows = 128;       // pool rows per large-M tile
+constexpr int kLargeMinRows = 65;     // experts with more rows than one small tile go large
 constexpr int kL1SlabCh = 128;        // intermediate channels per L1 workgroup (gate+up = 256 rows)
 constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgroup
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
@@ -143,5 +144,7 @@ namespace mm {
 hipError_t launch_route(const Args& a, hipStream_t s);
 hipError_t launch_l1_small(const Args& a, hipStream_t s);
 hipError_t launch_l2_small(const Args& a, hipStream_t s);
+hipError_t launch_l1_large(const Args& a, hipStream_t s);
+hipError_t launch_l2_large(const Args& a, hipStream_t s);
 hipError_t launch_combine(const Args& a, hipStream_t s);
 }  // namespace mm

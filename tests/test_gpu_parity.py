@@ -61,6 +61,13 @@ def test_small_problem_full_parity(name):
     _full_check(spec, synth.make_problem(spec))
 
 
+@pytest.mark.parametrize("flags", [1, 2], ids=["small_only", "large_only"])
+@pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile"])
+def test_forced_tile_class(name, flags):
+    spec = SMALL[name]
+    _full_check(spec, synth.make_problem(spec), flags)
+
+
 def test_all_tokens_on_one_expert():
     spec = synth.Spec(150, 512, 256, 8, 1, seed=110, weight_set=110)
     _full_check(spec, _custom(spec, idx=np.full((150, 1), 5)))

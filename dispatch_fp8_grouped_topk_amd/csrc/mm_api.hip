@@ -84,6 +84,20 @@ int check_device() {
   return st == 1 ? MEGA_MOE_OK : MEGA_MOE_ERR_UNSUPPORTED_DEVICE;
 }
 
+// Per-device compute-unit count (0 = not yet queried).
+std::atomic<int> g_num_cus[64];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = g_num_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_num_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 inline bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
 
 }  // namespace
@@ -185,6 +199,12 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;
   a.max_tiles_l = L.max_tiles_l;
+  // the large-M kernels address token rows with 32-bit byte offsets: larger problems go small
+  if ((uint64_t)a.T * (uint64_t)a.H >= (1ull << 32) || (uint64_t)a.P * (uint64_t)a.I >= (1ull << 32))
+    a.tile_mode = 1;
+  const int cus = device_cus();
+  if (cus <= 0) return MEGA_MOE_ERR_HIP;
+  a.large_grid = cus < 8 ? 8 : cus / 8 * 8;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> bool {

@@ -13,11 +13,19 @@ constexpr int kMaxExperts = 8192;     // LDS arrays of the scan kernel hold one 
 constexpr int kMaxTopk = 64;
 constexpr int kRouteBlock = 256;      // pairs per dispatch workgroup
 constexpr int kSmallRows = 64;        // pool rows per small-M tile (4 MFMA column groups of 16)
-constexpr int kLargeRows = 128;       // pool rows per large-M tile
+constexpr int kLargeRows = 256;       // most pool rows per large-M tile
 constexpr int kLargeMinRows = 65;     // experts with more rows than one small tile go large
 constexpr int kL1SlabCh = 128;        // intermediate channels per L1 workgroup (gate+up = 256 rows)
 constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgroup
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
+
+// Rows per large-M tile of an expert with c rows: the rows are split into ceil(c / 256) tiles
+// of equal height, rounded up to a multiple of 16 (the last tile takes the remainder).
+__host__ __device__ inline int large_tile_rows(int c) {
+  const int n = (c + kLargeRows - 1) / kLargeRows;
+  const int per = n ? (c + n - 1) / n : 0;
+  return (per + 15) & ~15;
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -58,6 +66,7 @@ struct Args {
   int tile_mode;        // 0 auto, 1 small only, 2 large only
   int large_min_rows;   // auto mode: experts with at least this many rows use the large class
   int max_tiles_s, max_tiles_l;
+  int large_grid;       // workgroups of the persistent large-M kernels (multiple of 8)
 };
 
 // ------------------------------------------------------------------------------------------

@@ -2,18 +2,28 @@
 // batches), where one weight slab is reused by many token rows.
 //
 // Orientation as in the small-M kernels (weight rows = MFMA M side, tokens = N side) and the
-// same workgroup decomposition (L1: one expert x one 128-channel slab, i.e. 256 w1 rows;
-// L2: one expert x 256 output columns), with 128 pool rows per tile and four waves.  Each wave
-// owns 64 weight rows (for L1 two 16-row gate tiles and the two matching up tiles, so SwiGLU
-// stays lane-local) against all 128 tokens: 32 MFMAs per K block, 128 float32 accumulators.
+// same slab decomposition (L1: one expert x one 128-channel slab, i.e. 256 w1 rows, gate and up;
+// L2: one expert x 256 output columns).  A tile holds up to 256 pool rows of one expert; the
+// route kernel splits an expert's rows into equal tiles of at most 256 (rounded up to 16).
 //
-// Operand paths are chosen by reuse.  A wave's weight rows are private to it, so they stream
-// from memory straight into registers, one K block ahead, without touching LDS.  The token
-// tile is needed by all four waves, so each K block of it is staged once in LDS with
-// global_load_lds_dwordx4 (three K blocks in flight, 16-byte chunk c of row r stored at slot
-// c ^ (r & 7) so the operand reads spread over the LDS banks), together with the per-row
-// activation scales.  Per K block the LDS carries 16 KB in and 64 KB out, well inside its
-// bandwidth at full MFMA rate.
+// Workgroup: 8 waves, two per SIMD, so that one wave's LDS reads and promotion arithmetic
+// overlap the other's MFMAs.  Wave w owns weight rows of group wm = w & 3 (64 rows: for L1 two
+// 16-row gate tiles and the two matching up tiles, so SwiGLU stays lane-local) and the 16-token
+// column groups g = 2i + (w >> 2) of the tile.  The kernels are instantiated per number of
+// column groups per wave (1..8), so a ragged tile costs at most one padded group per wave.
+//
+// Both operands and their scales are staged through LDS with global_load_lds_dwordx4 /
+// global_load_lds_dword (no VGPRs in flight), in a two-deep ring of 128-K blocks: block kb+1 is
+// fetched while block kb is multiplied.  16-byte chunk c of an FP8 row r sits at slot
+// c ^ (r & 7) (FP4 rows of 64 bytes: c ^ ((r >> 1) & 3)), which spreads the operand reads of
+// 16 consecutive rows over all LDS banks.  FP8 recipe: each MFMA covers exactly one 128-K scale
+// block and is promoted into the float accumulators with (activation scale x weight scale)
+// one column group later, off the MFMA's critical path.  MXFP4 recipe: the UE8M0 scales go to
+// the MFMA, which accumulates directly.
+//
+// The grid is persistent: each workgroup walks the (tile, slab) items with a stride of the
+// grid, and the 32 workgroups resident on one XCD take consecutive items, i.e. the slabs of
+// the same one or two token tiles, which then share those token rows in the XCD's L2.
 //
 // The epilogues are those of the small-M kernels: fused SwiGLU / clamp / top-k weight / group
 // amax / scale / E4M3 cast after L1 (design page section 10.1), BF16 slot rows after L2
@@ -24,27 +34,25 @@ namespace mm {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTok = kLargeRows;              // 128 pool rows per tile
-constexpr int kNS = kTok / 16;                // token column groups (all 8 per wave)
-constexpr int kStages = 3;
+constexpr int kTok = kLargeRows;              // pool rows per tile (256)
+constexpr int kWRows = 256;                   // weight rows per tile
 
 struct Stage {
-  uint8_t x[kTok * 128];                      // token rows of the K block (E4M3), swizzled
-  uint32_t sx[kTok];                          // per-token scale word (f32 bits | 4 x UE8M0)
+  uint8_t w[kWRows * 128];                    // weight rows of the K block (E4M3, or E2M1 in 64 B)
+  uint8_t x[kTok * 128];                      // token rows of the K block (E4M3)
+  // per 32-row block b: words [64b, 64b+32) = scale words of token rows 32b.., words
+  // [64b+32, 64b+64) = MXFP4 scale words (4 x UE8M0) of weight rows 32b..
+  uint32_t scl[2 * kTok];
 };
 
 struct Lds {
-  Stage st[kStages];
-  int rowsrc[kTok];
-  float red[4][kTok];                         // per wave (weight-row group): amax per token
-  float wsc[2][kMaxKBlocks];                  // FP8 recipe: float weight scales of the K blocks
+  Stage st[2];
+  int rowsrc[kTok];                           // source row of each tile row (token or pool row)
+  float red[4][kTok];                         // FP8 L1 epilogue: amax per (row group, token)
+  float wsc[2][kMaxKBlocks];                  // FP8 recipe: weight-block scales per K block
 };
-
-// per-wave LDS-direct load instructions per stage (vmcnt bookkeeping): 4 x 1 KB of token rows
-// and one scale-word instruction
-constexpr int kDmaPerStage = 5;
 
 // LDS-direct loads: each active lane fetches `size` bytes from its global address into
 // consecutive LDS bytes starting at the wave-uniform `lds` (lane i at lds + size*i).
@@ -55,19 +63,15 @@ __device__ __forceinline__ void lds_load4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt with vmcnt = N and no wait on expcnt / lgkmcnt (gfx9 encoding)
-  static_assert(N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0) without waiting on expcnt / lgkmcnt (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
 
-// Workgroup barrier for the K pipeline.  Unlike __syncthreads() it carries no memory fence,
-// whose release semantics would wait for every outstanding LDS-direct load (vmcnt(0)) and so
-// drain the prefetch queue at each K block.  Ordering is explicit instead: each wave waits for
-// its own loads of the block about to be read (wait_vmcnt) before arriving, LDS-direct writes
-// are complete in LDS once counted, and the empty asm statements stop the compiler from
-// moving LDS accesses across the barrier.
+// Workgroup barrier for the K pipeline.  Unlike __syncthreads() it carries no memory fence;
+// ordering is explicit instead: each wave waits for its own LDS-direct loads of the block about
+// to be read (wait_vmcnt0) before arriving, such writes are complete in LDS once counted, and
+// the empty asm statements stop the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -85,299 +89,320 @@ __device__ __forceinline__ v8i read_fp8_rows(const uint8_t* tile, int row, int l
   return r;
 }
 
-// Token-tile sources of one wave: rows 32w + 8j + lane/8 (j = 0..3), chunk (lane%8)^(lane/8),
-// and the scale word of row 32w + lane (lanes < 32).
-struct TokSrc {
-  const uint8_t* x[4];
-  const uint32_t* sx;
+__device__ __forceinline__ v8i read_fp4_rows(const uint8_t* tile, int row, int lg) {
+  const v4i lo = *reinterpret_cast<const v4i*>(tile + row * 64 + 16 * (lg ^ ((row >> 1) & 3)));
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+__device__ __forceinline__ int scl_tok(int row) { return 64 * (row >> 5) + (row & 31); }
+__device__ __forceinline__ int scl_w(int row) { return 64 * (row >> 5) + 32 + (row & 31); }
+
+// Global sources of one wave's share of a stage, as 32-bit byte offsets from wave-uniform bases
+// (the operand tensors are below 4 GiB; the host routes larger problems to the small class).
+// FP8 weights: rows 32w + 8j + lane/8 (j < 4); E2M1 weights: rows 32w + 16j + lane/4 (j < 2);
+// tokens: rows 32w + 8j + lane/8 (j < 4); scale word: token row 32w + lane (lanes < 32) or
+// weight row 32w + lane - 32 (lanes >= 32, MXFP4 only).
+struct Src {
+  const uint8_t* wb;
+  const uint8_t* xb;
+  const uint8_t* sb;                          // lane's scale base (token scales or weight scales)
+  uint32_t wo[4];
+  uint32_t xo[4];
+  uint32_t so;
+  int wkb;                                    // bytes per K block of a weight row
 };
 
-__device__ __forceinline__ void issue_tokens(Stage& S, const TokSrc& src, int kb, int w, int lane) {
-  uint8_t* xd = S.x + w * 32 * 128;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lds_load16(src.x[j] + (size_t)kb * 128, xd + j * 1024);
-  if (lane < 32) lds_load4(src.sx + kb, &S.sx[32 * w]);
-}
-
-__device__ __forceinline__ TokSrc token_srcs(const uint8_t* base, size_t row_bytes, const uint32_t* sc,
-                                             size_t sc_words, const int* rowsrc, int w, int lane) {
-  TokSrc t;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * w + 8 * j + (lane >> 3);
-    t.x[j] = base + (size_t)rowsrc[row] * row_bytes + 16 * ((lane & 7) ^ (lane >> 3));
-  }
-  t.sx = sc + (size_t)rowsrc[32 * w + (lane & 31)] * sc_words;
-  return t;
-}
-
-// Weight operand of one 16-row tile for K block kb (the lane's row pointer `row`).
+// tok: this wave's token rows are used by the tile (the first 32 NG rows are; waves past
+// them only fetch weights).
 template <int R>
-__device__ __forceinline__ v8i load_w(const uint8_t* row, int kb, int lg) {
-  if (R == 0) return load_fp8_operand(row + 128 * kb, lg);
-  return load_fp4_operand(row + 64 * kb, lg);
-}
-
-// The K loop shared by L1 and L2: acc[rt][s] (+)= the wave's 4 weight tiles x the 8 token
-// groups.  wrow[rt]: the lane's weight row for tile rt (E4M3 or E2M1 bytes).  FP8 recipe:
-// L.wsc[wsel[rt]][kb] is tile rt's float weight scale for K block kb, and each MFMA (one
-// 128-K scale block) is promoted into acc with (activation scale x weight scale).
-// MXFP4 recipe: wsf[rt] points at the lane's UE8M0 scale bytes (row, 4kb + lane/16).
-// One K block of the loop below: wait for / retire the pipeline stages, prefetch the next
-// weight block into An (when there is one) and the token block kb+2 into LDS, then multiply.
-template <int R>
-__device__ __forceinline__ void k_step(Lds& L, const TokSrc& tsrc, const uint8_t* const wrow[4],
-                                       const uint8_t* const wsf[4], const int wsel[4], int KB, int kb,
-                                       const v8i A[4], const int sw[4], v8i An[4], int swn[4],
-                                       v4f acc[4][kNS], int w, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-  // outstanding: [tokens kb] [weights kb] [tokens kb+1]; keep the newest stage in flight
-  if (kb + 1 < KB) wait_vmcnt<kDmaPerStage>();
-  else wait_vmcnt<0>();
-  pipeline_barrier();                    // token block kb landed for all waves; kb-1 retired
-  if (kb + 1 < KB) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      An[rt] = load_w<R>(wrow[rt], kb + 1, lg);
-      if (R == 1) swn[rt] = wsf[rt][4 * (kb + 1)];
-    }
-  }
-  if (kb + 2 < KB) issue_tokens(L.st[(kb + 2) % kStages], tsrc, kb + 2, w, lane);
-  const Stage& S = L.st[kb % kStages];
-  float cw[4];
+__device__ __forceinline__ void issue_stage(Stage& S, const Src& s, int kb, int w, int lane, bool tok) {
+  const uint8_t* wk = s.wb + (size_t)kb * s.wkb;
+  const uint8_t* xk = s.xb + (size_t)kb * 128;
   if (R == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
+    for (int j = 0; j < 4; ++j) lds_load16(wk + s.wo[j], S.w + (32 * w + 8 * j) * 128);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_load16(wk + s.wo[j], S.w + (32 * w + 16 * j) * 64);
   }
-  // token group s+1 is read from LDS while group s is multiplied
-  v8i B = read_fp8_rows(S.x, lr, lg);
-  uint32_t sxw = S.sx[lr];
+  if (tok) {
 #pragma unroll
-  for (int s = 0; s < kNS; ++s) {
-    v8i Bn;
-    uint32_t sxn = 0;
-    if (s + 1 < kNS) {
-      const int row = 16 * (s + 1) + lr;
-      Bn = read_fp8_rows(S.x, row, lg);
-      sxn = S.sx[row];
-    }
+    for (int j = 0; j < 4; ++j) lds_load16(xk + s.xo[j], S.x + (32 * w + 8 * j) * 128);
+  }
+  if (lane < 32 ? tok : R == 1) lds_load4(s.sb + (size_t)kb * 4 + s.so, &S.scl[64 * w]);
+}
+
+// The K loop shared by L1 and L2 for a wave with NG column groups: acc[rt][i] (+)= weight tile
+// rt x column group 2i + wn.  arow[rt]: the lane's LDS row of weight tile rt; wsel[rt]: its
+// FP8 weight-scale block (L.wsc row).
+template <int R, int NG>
+__device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4], const int wsel[4],
+                                       int KB, v4f acc[4][NG], int w, int wn, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const bool tok = w < NG;
+  issue_stage<R>(L.st[0], src, 0, w, lane, tok);
+  for (int kb = 0; kb < KB; ++kb) {
+    wait_vmcnt0();
+    pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
+    if (kb + 1 < KB) issue_stage<R>(L.st[(kb + 1) & 1], src, kb + 1, w, lane, tok);
+    const Stage& S = L.st[kb & 1];
+    v8i A[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) A[rt] = R == 0 ? read_fp8_rows(S.w, arow[rt], lg) : read_fp4_rows(S.w, arow[rt], lg);
     if (R == 0) {
-      const float sa = __uint_as_float(sxw);
-      v4f p[4];
+      float cw[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) p[rt] = mfma_fp8(A[rt], B);
+      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
+      v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
+      float sa = __uint_as_float(S.scl[scl_tok(16 * wn + lr)]);
+      float sp = 0.f;
+      v4f p[2][4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt][s] += p[rt] * (sa * cw[rt]);
+      for (int i = 0; i < NG; ++i) {
+        v8i Bn;
+        float san = 0.f;
+        if (i + 1 < NG) {
+          const int row = 16 * (2 * (i + 1) + wn) + lr;
+          Bn = read_fp8_rows(S.x, row, lg);
+          san = __uint_as_float(S.scl[scl_tok(row)]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          p[i & 1][rt] = mfma_fp8(A[rt], B);
+          if (i > 0) acc[rt][i - 1] += p[(i - 1) & 1][rt] * (sp * cw[rt]);
+        }
+        if (i > 0) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // the next group's LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sp = sa;
+        if (i + 1 < NG) {
+          B = Bn;
+          sa = san;
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += p[(NG - 1) & 1][rt] * (sp * cw[rt]);
     } else {
-      const int sx = (sxw >> (8 * lg)) & 0xFF;
+      int swv[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt][s] = mfma_fp4w_fp8(A[rt], B, acc[rt][s], sw[rt], sx);
-    }
-    if (s + 1 < kNS) {
-      B = Bn;
-      sxw = sxn;
+      for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[scl_w(arow[rt])] >> (8 * lg)) & 0xFF;
+      v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
+      uint32_t sxw = S.scl[scl_tok(16 * wn + lr)];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        v8i Bn;
+        uint32_t sxn = 0;
+        if (i + 1 < NG) {
+          const int row = 16 * (2 * (i + 1) + wn) + lr;
+          Bn = read_fp8_rows(S.x, row, lg);
+          sxn = S.scl[scl_tok(row)];
+        }
+        const int sx = (sxw >> (8 * lg)) & 0xFF;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_fp4w_fp8(A[rt], B, acc[rt][i], swv[rt], sx);
+        if (i + 1 < NG) {
+          B = Bn;
+          sxw = sxn;
+        }
+      }
     }
   }
 }
 
-// The K loop shared by L1 and L2: acc[rt][s] (+)= the wave's 4 weight tiles x the 8 token
-// groups.  wrow[rt]: the lane's weight row for tile rt (E4M3 or E2M1 bytes).  FP8 recipe:
-// L.wsc[wsel[rt]][kb] is tile rt's float weight scale for K block kb, and each MFMA (one
-// 128-K scale block) is promoted into acc with (activation scale x weight scale).  MXFP4
-// recipe: wsf[rt] points at the lane's UE8M0 scale bytes (row, 4kb + lane/16).  Two register
-// sets of weights alternate between even and odd K blocks, so the prefetch of block kb+1 is
-// only waited for when block kb+1 starts.
-template <int R>
-__device__ __forceinline__ void k_loop(Lds& L, const TokSrc& tsrc, const uint8_t* const wrow[4],
-                                       const uint8_t* const wsf[4], const int wsel[4], int KB,
-                                       v4f acc[4][kNS], int w, int lane) {
-  const int lg = lane >> 4;
-  v8i A0[4], A1[4];
-  int s0[4] = {0, 0, 0, 0}, s1[4] = {0, 0, 0, 0};
+// Per-lane global offsets of one wave's share of the token rows (tile rows 32w + 8j + lane/8).
+__device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, int w, int lane) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    A0[rt] = load_w<R>(wrow[rt], 0, lg);
-    if (R == 1) s0[rt] = wsf[rt][0];
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * w + 8 * j + (lane >> 3);
+    s.xo[j] = (uint32_t)rowsrc[r] * row_bytes + 16u * (uint32_t)((lane & 7) ^ (r & 7));
   }
-  issue_tokens(L.st[0], tsrc, 0, w, lane);
-  if (KB > 1) issue_tokens(L.st[1], tsrc, 1, w, lane);
-  for (int kb = 0; kb < KB; kb += 2) {
-    k_step<R>(L, tsrc, wrow, wsf, wsel, KB, kb, A0, s0, A1, s1, acc, w, lane);
-    if (kb + 1 < KB) k_step<R>(L, tsrc, wrow, wsf, wsel, KB, kb + 1, A1, s1, A0, s0, acc, w, lane);
+}
+
+// Per-lane global offsets of one wave's share of the weight rows; grow(r) maps a tile row to
+// the weight row within the expert.
+template <int R, class F>
+__device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_bytes, int w, int lane) {
+  if (R == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * w + 8 * j + (lane >> 3);
+      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 32 * w + 16 * j + (lane >> 2);
+      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 3) ^ ((r >> 1) & 3));
+    }
+    s.wo[2] = s.wo[3] = 0;
   }
 }
 
 // ------------------------------------------------------------------------------------ L1
-template <int R>
-__device__ __forceinline__ void l1_large_tile(const Args& a, int e, int m0, int cnt, int slab, Lds& L) {
+template <int R, int NG>
+__device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int cnt, int slab, Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 3, wn = w >> 2;
   const int H = a.H, I = a.I, KB = H / 128;
-  const int off = a.offset[e] + m0;
 
-  if (tid < kTok) L.rowsrc[tid] = a.pool_src[off + (tid < cnt ? tid : cnt - 1)] / a.k;
+  Src src;
+  src.wkb = R == 0 ? 128 : 64;
+  src.wb = a.l1_w + (size_t)e * 2 * I * (R == 0 ? H : H / 2);
+  src.xb = a.x;
+  const auto grow = [&](int r) { return r < 128 ? 128 * slab + r : I + 128 * slab + (r - 128); };
+  weight_offsets<R>(src, grow, R == 0 ? H : H / 2, w, lane);
+  token_offsets(src, L.rowsrc, H, w, lane);
   if (R == 0) {
-    // float scales of the gate block (row 0) and the up block (row 1) for every K block
-    const float* sfw = static_cast<const float*>(a.l1_sf) + (size_t)e * (2 * I / 128) * KB;
-    for (int i = tid; i < 2 * KB; i += kThreads)
-      L.wsc[i / KB][i % KB] = sfw[(size_t)(i < KB ? slab : I / 128 + slab) * KB + i % KB];
+    src.sb = static_cast<const uint8_t*>(a.x_sf);
+    src.so = (uint32_t)L.rowsrc[32 * w + (lane & 31)] * (uint32_t)(KB * 4);
+  } else if (lane < 32) {
+    src.sb = static_cast<const uint8_t*>(a.x_sf);
+    src.so = (uint32_t)L.rowsrc[32 * w + lane] * (uint32_t)(H / 32);
+  } else {
+    src.sb = static_cast<const uint8_t*>(a.l1_sf) + (size_t)e * 2 * I * (H / 32);
+    src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(H / 32);
   }
-  __syncthreads();
-
-  const TokSrc tsrc = token_srcs(a.x, H, static_cast<const uint32_t*>(a.x_sf), H / 128, L.rowsrc, w, lane);
-  const size_t wstride = R == 0 ? (size_t)H : (size_t)H / 2;
-  const uint8_t* wrow[4];
-  const uint8_t* wsf[4];
+  int arow[4], wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const int row = (rt < 2 ? 0 : I) + 128 * slab + 32 * w + 16 * (rt & 1) + lr;
-    wrow[rt] = a.l1_w + ((size_t)e * 2 * I + row) * wstride;
-    wsf[rt] = static_cast<const uint8_t*>(a.l1_sf) + ((size_t)e * 2 * I + row) * (H / 32) + lg;
+    arow[rt] = (rt < 2 ? 0 : 128) + 32 * wm + 16 * (rt & 1) + lr;
+    wsel[rt] = rt < 2 ? 0 : 1;
   }
-  const int wsel[4] = {0, 0, 1, 1};
 
-  v4f acc[4][kNS];
+  v4f acc[4][NG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) acc[rt][s] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R>(L, tsrc, wrow, wsf, wsel, KB, acc, w, lane);
+    for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  k_loop<R, NG>(L, src, arow, wsel, KB, acc, w, wn, lane);
 
   // ---------------- epilogue: SwiGLU, clamp, top-k weight, group amax, scale, E4M3 cast
-  // acc[i][s][r] (gate) and acc[2+i][s][r] (up) are channel 32w + 16i + 4lg + r of the slab
-  // for tile row 16s + lr.
+  // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 16t + 4lg + r of the slab
+  // for tile row 16(2i + wn) + lr.
   const bool do_clamp = a.clamp > 0.f;
-  float v[kNS][2][4];
+  float v[NG][2][4];
 #pragma unroll
-  for (int s = 0; s < kNS; ++s) {
-    const int col = 16 * s + lr;
+  for (int i = 0; i < NG; ++i) {
+    const int col = 16 * (2 * i + wn) + lr;
     const float wt = col < cnt ? a.w_pool[off + col] : 0.f;
     float am = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float g = acc[i][s][r], u = acc[2 + i][s][r];
+        const float g = acc[t][i][r], u = acc[2 + t][i][r];
         float sv = g / (1.0f + expf(-g)) * u;
         if (do_clamp) sv = fminf(fmaxf(sv, -a.clamp), a.clamp);
         const float x = sv * wt;
-        v[s][i][r] = x;
+        v[i][t][r] = x;
         am = fmaxf(am, fabsf(x));
       }
     am = fmaxf(am, __shfl_xor(am, 16, 64));
     am = fmaxf(am, __shfl_xor(am, 32, 64));
     if (R == 0) {
-      if (lg == 0) L.red[w][col] = am;
+      if (lg == 0) L.red[wm][col] = am;
     } else {
       // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
       const uint32_t code = ue8m0_for_amax(am);
       const int ex = 127 - (int)code;
       const bool valid = col < cnt;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int t = 0; t < 2; ++t) {
         uint32_t q = 0;
         if (am > 0.f)
-          q = pack_fp8x4(clamp448(ldexpf(v[s][i][0], ex)), clamp448(ldexpf(v[s][i][1], ex)),
-                         clamp448(ldexpf(v[s][i][2], ex)), clamp448(ldexpf(v[s][i][3], ex)));
+          q = pack_fp8x4(clamp448(ldexpf(v[i][t][0], ex)), clamp448(ldexpf(v[i][t][1], ex)),
+                         clamp448(ldexpf(v[i][t][2], ex)), clamp448(ldexpf(v[i][t][3], ex)));
         if (valid)
-          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
+          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
       }
       if (valid && lg == 0)
-        static_cast<uint8_t*>(a.inter_sf)[(size_t)(off + col) * (I / 32) + 4 * slab + w] = (uint8_t)code;
+        static_cast<uint8_t*>(a.inter_sf)[(size_t)(off + col) * (I / 32) + 4 * slab + wm] = (uint8_t)code;
     }
   }
   if (R == 0) {
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) {
-      const int col = 16 * s + lr;
+    for (int i = 0; i < NG; ++i) {
+      const int col = 16 * (2 * i + wn) + lr;
       const float amax = fmaxf(fmaxf(L.red[0][col], L.red[1][col]), fmaxf(L.red[2][col], L.red[3][col]));
       const float sf = amax / 448.0f;
       const bool valid = col < cnt;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int t = 0; t < 2; ++t) {
         uint32_t q = 0;
         if (sf > 0.f)
-          q = pack_fp8x4(clamp448(v[s][i][0] / sf), clamp448(v[s][i][1] / sf),
-                         clamp448(v[s][i][2] / sf), clamp448(v[s][i][3] / sf));
+          q = pack_fp8x4(clamp448(v[i][t][0] / sf), clamp448(v[i][t][1] / sf),
+                         clamp448(v[i][t][2] / sf), clamp448(v[i][t][3] / sf));
         if (valid)
-          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
+          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
       }
-      if (valid && w == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)(off + col) * (I / 128) + slab] = sf;
+      if (valid && wm == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)(off + col) * (I / 128) + slab] = sf;
     }
   }
-}
-
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_l1_large(Args a) {
-  __shared__ __attribute__((aligned(1024))) Lds L;
-  const int q = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int n_slabs = a.I / kL1SlabCh;
-  const int slab = q / a.max_tiles_l;
-  const int tile = q - slab * a.max_tiles_l;
-  if (slab >= n_slabs || tile >= a.hdr[kHdrTilesLarge]) return;
-  const int2 td = a.tiles_l[tile];
-  const int rem = a.count[td.x] - td.y;
-  l1_large_tile<R>(a, td.x, td.y, rem < kTok ? rem : kTok, slab, L);
 }
 
 // ------------------------------------------------------------------------------------ L2
-template <int R>
-__device__ __forceinline__ void l2_large_tile(const Args& a, int e, int m0, int cnt, int slab, Lds& L) {
+template <int R, int NG>
+__device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int cnt, int slab, Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 3, wn = w >> 2;
   const int H = a.H, I = a.I, KB = I / 128;
-  const int off = a.offset[e] + m0;
 
-  if (tid < kTok) L.rowsrc[tid] = off + (tid < cnt ? tid : cnt - 1);   // pool row feeding token row
+  Src src;
+  src.wkb = R == 0 ? 128 : 64;
+  src.wb = a.l2_w + (size_t)e * H * (R == 0 ? I : I / 2);
+  src.xb = a.inter_q;
+  // tile rows past H (H a multiple of 128 but not of 256) repeat valid rows; their results drop
+  const auto grow = [&](int r) { const int g = kWRows * slab + r; return g < H ? g : g - 128; };
+  weight_offsets<R>(src, grow, R == 0 ? I : I / 2, w, lane);
+  token_offsets(src, L.rowsrc, I, w, lane);
   if (R == 0) {
-    // float scales of the slab's two 128-row blocks of w2 for every K block (a block past H,
-    // when H is not a multiple of 256, repeats the last one; its waves drop their results)
-    const float* sfw = static_cast<const float*>(a.l2_sf) + (size_t)e * (H / 128) * KB;
-    for (int i = tid; i < 2 * KB; i += kThreads) {
-      int blk = 2 * slab + i / KB;
-      blk = blk < H / 128 ? blk : H / 128 - 1;
-      L.wsc[i / KB][i % KB] = sfw[(size_t)blk * KB + i % KB];
-    }
+    src.sb = static_cast<const uint8_t*>(a.inter_sf);
+    src.so = (uint32_t)L.rowsrc[32 * w + (lane & 31)] * (uint32_t)(KB * 4);
+  } else if (lane < 32) {
+    src.sb = static_cast<const uint8_t*>(a.inter_sf);
+    src.so = (uint32_t)L.rowsrc[32 * w + lane] * (uint32_t)(I / 32);
+  } else {
+    src.sb = static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32);
+    src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(I / 32);
   }
-  __syncthreads();
-
-  // the wave's output columns nbase .. nbase+63 (w2 rows); a wave past H (when H is not a
-  // multiple of 256) still stages its share of the token tile but computes from valid rows
-  // and drops its results
-  const int nbase = kL2SlabRows * slab + 64 * w;
-  const bool active = nbase < H;                 // wave-uniform: H is a multiple of 128
-  const int nrow0 = active ? nbase : H - 64;
-  const TokSrc tsrc = token_srcs(a.inter_q, I, static_cast<const uint32_t*>(a.inter_sf), I / 128,
-                                 L.rowsrc, w, lane);
-  const size_t wstride = R == 0 ? (size_t)I : (size_t)I / 2;
-  const uint8_t* wrow[4];
-  const uint8_t* wsf[4];
+  int arow[4], wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const size_t row = (size_t)e * H + nrow0 + 16 * rt + lr;
-    wrow[rt] = a.l2_w + row * wstride;
-    wsf[rt] = static_cast<const uint8_t*>(a.l2_sf) + row * (I / 32) + lg;
+    arow[rt] = 64 * wm + 16 * rt + lr;
+    wsel[rt] = wm >> 1;
   }
-  const int wsel[4] = {w >> 1, w >> 1, w >> 1, w >> 1};
 
-  v4f acc[4][kNS];
+  v4f acc[4][NG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) acc[rt][s] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R>(L, tsrc, wrow, wsf, wsel, KB, acc, w, lane);
+    for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  k_loop<R, NG>(L, src, arow, wsel, KB, acc, w, wn, lane);
 
-  if (!active) return;
+  const int nbase = kWRows * slab + 64 * wm;
+  if (nbase >= H) return;                        // wave-uniform: H is a multiple of 128
   // ---------------- epilogue: BF16 rows into the pair-ordered slot buffer
 #pragma unroll
-  for (int s = 0; s < kNS; ++s) {
-    const int col = 16 * s + lr;
+  for (int i = 0; i < NG; ++i) {
+    const int col = 16 * (2 * i + wn) + lr;
     if (col >= cnt) continue;
     uint16_t* dst = a.slot + (size_t)a.pool_src[off + col] * H + nbase + 4 * lg;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const v4f o = acc[rt][s];
+      const v4f o = acc[rt][i];
       uint2 pk;
       pk.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
       pk.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
@@ -386,37 +411,80 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int m0, int 
   }
 }
 
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_l2_large(Args a) {
-  __shared__ __attribute__((aligned(1024))) Lds L;
-  const int q = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int n_slabs = (a.H + kL2SlabRows - 1) / kL2SlabRows;
-  const int slab = q / a.max_tiles_l;
-  const int tile = q - slab * a.max_tiles_l;
-  if (slab >= n_slabs || tile >= a.hdr[kHdrTilesLarge]) return;
+// ------------------------------------------------------------------------------------ kernels
+// Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
+template <int R, bool L1>
+__device__ __forceinline__ void run_item(const Args& a, int q, int n_slabs, Lds& L) {
+  const int tid = threadIdx.x;
+  const int tile = q / n_slabs, slab = q - tile * n_slabs;
   const int2 td = a.tiles_l[tile];
-  const int rem = a.count[td.x] - td.y;
-  l2_large_tile<R>(a, td.x, td.y, rem < kTok ? rem : kTok, slab, L);
+  const int e = td.x, m0 = td.y;
+  const int c = a.count[e];
+  const int cnt = min(large_tile_rows(c), c - m0);
+  const int off = a.offset[e] + m0;
+  const int H = a.H, I = a.I;
+
+  __syncthreads();                             // the previous item is done with the LDS
+  if (tid < kTok) {
+    const int pr = off + (tid < cnt ? tid : cnt - 1);
+    L.rowsrc[tid] = L1 ? a.pool_src[pr] / a.k : pr;
+  }
+  if (R == 0) {
+    if (L1) {
+      // float scales of the gate block (row 0) and the up block (row 1) for every K block
+      const int KB = H / 128;
+      const float* sfw = static_cast<const float*>(a.l1_sf) + (size_t)e * (2 * I / 128) * KB;
+      for (int i = tid; i < 2 * KB; i += kThreads)
+        L.wsc[i / KB][i % KB] = sfw[(size_t)(i < KB ? slab : I / 128 + slab) * KB + i % KB];
+    } else {
+      // float scales of the slab's two 128-row blocks of w2 (clamped past H) for every K block
+      const int KB = I / 128;
+      const float* sfw = static_cast<const float*>(a.l2_sf) + (size_t)e * (H / 128) * KB;
+      for (int i = tid; i < 2 * KB; i += kThreads) {
+        int blk = 2 * slab + i / KB;
+        blk = blk < H / 128 ? blk : H / 128 - 1;
+        L.wsc[i / KB][i % KB] = sfw[(size_t)blk * KB + i % KB];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nw = ((cnt + 15) / 16 + 1) / 2;    // column groups per wave
+  switch (nw) {
+#define MM_CASE(n)                                                 \
+  case n:                                                          \
+    if (L1) l1_large_tile<R, n>(a, e, off, cnt, slab, L);          \
+    else l2_large_tile<R, n>(a, e, off, cnt, slab, L);             \
+    break;
+    MM_CASE(1) MM_CASE(2) MM_CASE(3) MM_CASE(4) MM_CASE(5) MM_CASE(6) MM_CASE(7)
+    default: MM_CASE(8)
+#undef MM_CASE
+  }
 }
 
-inline int round8(long v) { return (int)((v + 7) / 8 * 8); }
+// Persistent item loop: item q = (tile q / n_slabs, slab q % n_slabs).  Round r gives XCD x
+// (hardware workgroup id mod 8) the items r*G + x*(G/8) + j for its workgroups j.
+template <int R, bool L1>
+__global__ __launch_bounds__(kThreads) void k_large(Args a) {
+  __shared__ __attribute__((aligned(1024))) Lds L;
+  const int n_slabs = L1 ? a.I / kL1SlabCh : (a.H + kWRows - 1) / kWRows;
+  const int n_items = a.hdr[kHdrTilesLarge] * n_slabs;
+  const int G = gridDim.x, per = G >> 3;
+  const int mine = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  for (int base = 0; base + mine < n_items; base += G) run_item<R, L1>(a, base + mine, n_slabs, L);
+}
+
+template <bool L1>
+hipError_t launch_large(const Args& a, hipStream_t s) {
+  if (a.max_tiles_l == 0 || a.tile_mode == 1) return hipSuccess;
+  if (a.recipe == 0) hipLaunchKernelGGL((k_large<0, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_large<1, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace
 
-hipError_t launch_l1_large(const Args& a, hipStream_t s) {
-  if (a.max_tiles_l == 0 || a.tile_mode == 1) return hipSuccess;
-  const int grid = round8((long)a.max_tiles_l * (a.I / kL1SlabCh));
-  if (a.recipe == 0) hipLaunchKernelGGL(k_l1_large<0>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_l1_large<1>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_l2_large(const Args& a, hipStream_t s) {
-  if (a.max_tiles_l == 0 || a.tile_mode == 1) return hipSuccess;
-  const int grid = round8((long)a.max_tiles_l * ((a.H + kL2SlabRows - 1) / kL2SlabRows));
-  if (a.recipe == 0) hipLaunchKernelGGL(k_l2_large<0>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_l2_large<1>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
+hipError_t launch_l1_large(const Args& a, hipStream_t s) { return launch_large<true>(a, s); }
+hipError_t launch_l2_large(const Args& a, hipStream_t s) { return launch_large<false>(a, s); }
 
 }  // namespace mm

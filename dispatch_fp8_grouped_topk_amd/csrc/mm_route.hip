@@ -130,7 +130,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
       const int bs = carry_s + inc_s - nts;
       for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);
       const int bl = carry_l + inc_l - ntl;
-      for (int i = 0; i < ntl; ++i) a.tiles_l[bl + i] = make_int2(e, i * kLargeRows);
+      const int per = large_tile_rows(c);
+      for (int i = 0; i < ntl; ++i) a.tiles_l[bl + i] = make_int2(e, i * per);
     }
     carry += tot;
     carry_s += tot_s;

@@ -14,7 +14,10 @@ constexpr int kMaxTopk = 64;
 constexpr int kRouteBlock = 256;      // pairs per dispatch workgroup
 constexpr int kSmallRows = 64;        // pool rows per small-M tile (4 MFMA column groups of 16)
 constexpr int kLargeRows = 256;       // most pool rows per large-M tile
-constexpr int kLargeMinRows = 65;     // experts with more rows than one small tile go large
+// Auto mode: experts with at least this many rows use the large-M class.  Measured on MI355X,
+// the persistent large-M kernel (three-deep operand ring for small tiles) is at least as fast
+// as the small-M kernels down to single-row experts, so it takes every expert.
+constexpr int kLargeMinRows = 1;
 constexpr int kL1SlabCh = 128;        // intermediate channels per L1 workgroup (gate+up = 256 rows)
 constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgroup
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)

@@ -13,8 +13,9 @@
 // column groups per wave (1..8), so a ragged tile costs at most one padded group per wave.
 //
 // Both operands and their scales are staged through LDS with global_load_lds_dwordx4 /
-// global_load_lds_dword (no VGPRs in flight), in a two-deep ring of 128-K blocks: block kb+1 is
-// fetched while block kb is multiplied.  16-byte chunk c of an FP8 row r sits at slot
+// global_load_lds_dword (no VGPRs in flight), in a ring of 128-K blocks: three deep for tiles of
+// up to 4 column groups per wave (blocks kb+1 and kb+2 in flight while kb is multiplied), two
+// deep above that, where the larger token tile leaves LDS room for two.  16-byte chunk c of an FP8 row r sits at slot
 // c ^ (r & 7) (FP4 rows of 64 bytes: c ^ ((r >> 1) & 3)), which spreads the operand reads of
 // 16 consecutive rows over all LDS banks.  FP8 recipe: each MFMA covers exactly one 128-K scale
 // block and is promoted into the float accumulators with (activation scale x weight scale)
@@ -39,20 +40,41 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTok = kLargeRows;              // pool rows per tile (256)
 constexpr int kWRows = 256;                   // weight rows per tile
 
-struct Stage {
-  uint8_t w[kWRows * 128];                    // weight rows of the K block (E4M3, or E2M1 in 64 B)
-  uint8_t x[kTok * 128];                      // token rows of the K block (E4M3)
-  // per 32-row block b: words [64b, 64b+32) = scale words of token rows 32b.., words
-  // [64b+32, 64b+64) = MXFP4 scale words (4 x UE8M0) of weight rows 32b..
-  uint32_t scl[2 * kTok];
+// Ring geometry for NG column groups per wave: a stage holds the 256 weight rows, the first
+// 32 NG token rows (128 bytes each, E2M1 weights use the first 64 of a weight row) and 512
+// scale words: per wave w, words [64w, 64w+32) are activation scale words in the order
+// (wn, lr, i) of the readers (see tok_scale_row) and words [64w+32, 64w+64) the MXFP4 scale
+// words (4 x UE8M0) of weight rows 32w...
+template <int NG>
+struct Ring {
+  static constexpr int kXRows = 32 * NG;
+  static constexpr int kStageBytes = kWRows * 128 + kXRows * 128 + 2048;
+  static constexpr int kStages = NG <= 4 ? 3 : 2;
+};
+constexpr int kRingBytes = Ring<4>::kStages * Ring<4>::kStageBytes > Ring<8>::kStages * Ring<8>::kStageBytes
+                               ? Ring<4>::kStages * Ring<4>::kStageBytes
+                               : Ring<8>::kStages * Ring<8>::kStageBytes;
+
+struct StageRef {
+  uint8_t* w;
+  uint8_t* x;
+  uint32_t* scl;
 };
 
+template <int NG>
+__device__ __forceinline__ StageRef stage_ref(uint8_t* ring, int s) {
+  uint8_t* b = ring + s * Ring<NG>::kStageBytes;
+  return StageRef{b, b + kWRows * 128, reinterpret_cast<uint32_t*>(b + kWRows * 128 + Ring<NG>::kXRows * 128)};
+}
+
 struct Lds {
-  Stage st[2];
+  uint8_t ring[kRingBytes];
   int rowsrc[kTok];                           // source row of each tile row (token or pool row)
+  int aux[kTok];                              // L1: top-k weight (f32 bits) / L2: slot row, per tile row
   float red[4][kTok];                         // FP8 L1 epilogue: amax per (row group, token)
   float wsc[2][kMaxKBlocks];                  // FP8 recipe: weight-block scales per K block
 };
+static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
 
 // LDS-direct loads: each active lane fetches `size` bytes from its global address into
 // consecutive LDS bytes starting at the wave-uniform `lds` (lane i at lds + size*i).
@@ -63,14 +85,9 @@ __device__ __forceinline__ void lds_load4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmcnt0() {
-  // s_waitcnt vmcnt(0) without waiting on expcnt / lgkmcnt (gfx9 encoding)
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-}
-
 // Workgroup barrier for the K pipeline.  Unlike __syncthreads() it carries no memory fence;
 // ordering is explicit instead: each wave waits for its own LDS-direct loads of the block about
-// to be read (wait_vmcnt0) before arriving, such writes are complete in LDS once counted, and
+// to be read (wait_block) before arriving, such writes are complete in LDS once counted, and
 // the empty asm statements stop the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
@@ -97,14 +114,18 @@ __device__ __forceinline__ v8i read_fp4_rows(const uint8_t* tile, int row, int l
   return r;
 }
 
-__device__ __forceinline__ int scl_tok(int row) { return 64 * (row >> 5) + (row & 31); }
+// Activation scale word d (0..255; wave d/32, lane d%32 of the scale load) belongs to token row
+// 16 (2i + wn) + lr with wn = d / 128, lr = (d / 8) % 16, i = d % 8, so that the reader (wn, lr)
+// finds the words of its column groups i = 0..7 at 8 consecutive positions, tok_scale_pos.
+__device__ __forceinline__ int tok_scale_row(int d) { return 16 * (2 * (d & 7) + (d >> 7)) + ((d >> 3) & 15); }
+__device__ __forceinline__ int tok_scale_pos(int wn, int lr) { return 64 * (4 * wn + (lr >> 2)) + 8 * (lr & 3); }
 __device__ __forceinline__ int scl_w(int row) { return 64 * (row >> 5) + 32 + (row & 31); }
 
 // Global sources of one wave's share of a stage, as 32-bit byte offsets from wave-uniform bases
 // (the operand tensors are below 4 GiB; the host routes larger problems to the small class).
 // FP8 weights: rows 32w + 8j + lane/8 (j < 4); E2M1 weights: rows 32w + 16j + lane/4 (j < 2);
-// tokens: rows 32w + 8j + lane/8 (j < 4); scale word: token row 32w + lane (lanes < 32) or
-// weight row 32w + lane - 32 (lanes >= 32, MXFP4 only).
+// tokens: rows 32w + 8j + lane/8 (j < 4); scale word: activation scale word 32w + lane (lanes <
+// 32) or weight row 32w + lane - 32 (lanes >= 32, MXFP4 only).
 struct Src {
   const uint8_t* wb;
   const uint8_t* xb;
@@ -115,10 +136,10 @@ struct Src {
   int wkb;                                    // bytes per K block of a weight row
 };
 
-// tok: this wave's token rows are used by the tile (the first 32 NG rows are; waves past
-// them only fetch weights).
+// tok: this wave's token rows are staged (the first 32 NG rows are; waves past them only fetch
+// weights and scales).  LDS-direct loads per wave and stage: FP8 4 + 4 tok + 1, MXFP4 2 + 4 tok + 1.
 template <int R>
-__device__ __forceinline__ void issue_stage(Stage& S, const Src& s, int kb, int w, int lane, bool tok) {
+__device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w, int lane, bool tok) {
   const uint8_t* wk = s.wb + (size_t)kb * s.wkb;
   const uint8_t* xk = s.xb + (size_t)kb * 128;
   if (R == 0) {
@@ -132,7 +153,26 @@ __device__ __forceinline__ void issue_stage(Stage& S, const Src& s, int kb, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) lds_load16(xk + s.xo[j], S.x + (32 * w + 8 * j) * 128);
   }
-  if (lane < 32 ? tok : R == 1) lds_load4(s.sb + (size_t)kb * 4 + s.so, &S.scl[64 * w]);
+  if (R == 1 || lane < 32) lds_load4(s.sb + (size_t)kb * 4 + s.so, S.scl + 64 * w);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N) without waiting on expcnt / lgkmcnt (gfx9 encoding)
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until this wave's loads of block kb have landed: with a three-deep ring the loads of
+// block kb+1 (if any) may stay in flight.
+template <int R, int NS>
+__device__ __forceinline__ void wait_block(bool newer, bool tok) {
+  if (NS == 3 && newer) {
+    if (tok) wait_vmcnt<R == 0 ? 9 : 7>();
+    else wait_vmcnt<R == 0 ? 5 : 3>();
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 // The K loop shared by L1 and L2 for a wave with NG column groups: acc[rt][i] (+)= weight tile
@@ -141,34 +181,48 @@ __device__ __forceinline__ void issue_stage(Stage& S, const Src& s, int kb, int 
 template <int R, int NG>
 __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4], const int wsel[4],
                                        int KB, v4f acc[4][NG], int w, int wn, int lane) {
+  constexpr int NS = Ring<NG>::kStages;
   const int lr = lane & 15, lg = lane >> 4;
   const bool tok = w < NG;
-  issue_stage<R>(L.st[0], src, 0, w, lane, tok);
+  const int tsp = tok_scale_pos(wn, lr);
+  issue_stage<R>(stage_ref<NG>(L.ring, 0), src, 0, w, lane, tok);
+  if (NS == 3 && KB > 1) issue_stage<R>(stage_ref<NG>(L.ring, 1), src, 1, w, lane, tok);
+  int cur = 0;                           // ring slot of block kb
   for (int kb = 0; kb < KB; ++kb) {
-    wait_vmcnt0();
+    wait_block<R, NS>(kb + 1 < KB, tok);
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
-    if (kb + 1 < KB) issue_stage<R>(L.st[(kb + 1) & 1], src, kb + 1, w, lane, tok);
-    const Stage& S = L.st[kb & 1];
+    {
+      const int ahead = kb + NS - 1;
+      int slot = cur + NS - 1;
+      slot = slot >= NS ? slot - NS : slot;
+      if (ahead < KB) issue_stage<R>(stage_ref<NG>(L.ring, slot), src, ahead, w, lane, tok);
+    }
+    const StageRef S = stage_ref<NG>(L.ring, cur);
+    cur = cur + 1 == NS ? 0 : cur + 1;
     v8i A[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) A[rt] = R == 0 ? read_fp8_rows(S.w, arow[rt], lg) : read_fp4_rows(S.w, arow[rt], lg);
+    // activation scale words of column groups 0..NG-1
+    uint32_t sw8[8];
+    {
+      const v4i lo = *reinterpret_cast<const v4i*>(S.scl + tsp);
+      sw8[0] = lo[0]; sw8[1] = lo[1]; sw8[2] = lo[2]; sw8[3] = lo[3];
+      if (NG > 4) {
+        const v4i hi = *reinterpret_cast<const v4i*>(S.scl + tsp + 4);
+        sw8[4] = hi[0]; sw8[5] = hi[1]; sw8[6] = hi[2]; sw8[7] = hi[3];
+      }
+    }
     if (R == 0) {
       float cw[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
       v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
-      float sa = __uint_as_float(S.scl[scl_tok(16 * wn + lr)]);
-      float sp = 0.f;
       v4f p[2][4];
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         v8i Bn;
-        float san = 0.f;
-        if (i + 1 < NG) {
-          const int row = 16 * (2 * (i + 1) + wn) + lr;
-          Bn = read_fp8_rows(S.x, row, lg);
-          san = __uint_as_float(S.scl[scl_tok(row)]);
-        }
+        if (i + 1 < NG) Bn = read_fp8_rows(S.x, 16 * (2 * (i + 1) + wn) + lr, lg);
+        const float sp = i > 0 ? __uint_as_float(sw8[i - 1]) : 0.f;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           p[i & 1][rt] = mfma_fp8(A[rt], B);
@@ -180,16 +234,13 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4]
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // the next group's LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the next group's LDS reads
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        sp = sa;
-        if (i + 1 < NG) {
-          B = Bn;
-          sa = san;
-        }
+        if (i + 1 < NG) B = Bn;
       }
+      const float sp = __uint_as_float(sw8[NG - 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += p[(NG - 1) & 1][rt] * (sp * cw[rt]);
     } else {
@@ -197,23 +248,14 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4]
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[scl_w(arow[rt])] >> (8 * lg)) & 0xFF;
       v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
-      uint32_t sxw = S.scl[scl_tok(16 * wn + lr)];
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         v8i Bn;
-        uint32_t sxn = 0;
-        if (i + 1 < NG) {
-          const int row = 16 * (2 * (i + 1) + wn) + lr;
-          Bn = read_fp8_rows(S.x, row, lg);
-          sxn = S.scl[scl_tok(row)];
-        }
-        const int sx = (sxw >> (8 * lg)) & 0xFF;
+        if (i + 1 < NG) Bn = read_fp8_rows(S.x, 16 * (2 * (i + 1) + wn) + lr, lg);
+        const int sx = (sw8[i] >> (8 * lg)) & 0xFF;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_fp4w_fp8(A[rt], B, acc[rt][i], swv[rt], sx);
-        if (i + 1 < NG) {
-          B = Bn;
-          sxw = sxn;
-        }
+        if (i + 1 < NG) B = Bn;
       }
     }
   }
@@ -265,10 +307,10 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   token_offsets(src, L.rowsrc, H, w, lane);
   if (R == 0) {
     src.sb = static_cast<const uint8_t*>(a.x_sf);
-    src.so = (uint32_t)L.rowsrc[32 * w + (lane & 31)] * (uint32_t)(KB * 4);
+    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)(KB * 4);
   } else if (lane < 32) {
     src.sb = static_cast<const uint8_t*>(a.x_sf);
-    src.so = (uint32_t)L.rowsrc[32 * w + lane] * (uint32_t)(H / 32);
+    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + lane)] * (uint32_t)(H / 32);
   } else {
     src.sb = static_cast<const uint8_t*>(a.l1_sf) + (size_t)e * 2 * I * (H / 32);
     src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(H / 32);
@@ -295,7 +337,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int col = 16 * (2 * i + wn) + lr;
-    const float wt = col < cnt ? a.w_pool[off + col] : 0.f;
+    const float wt = col < cnt ? __int_as_float(L.aux[col]) : 0.f;
     float am = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -370,10 +412,10 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   token_offsets(src, L.rowsrc, I, w, lane);
   if (R == 0) {
     src.sb = static_cast<const uint8_t*>(a.inter_sf);
-    src.so = (uint32_t)L.rowsrc[32 * w + (lane & 31)] * (uint32_t)(KB * 4);
+    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)(KB * 4);
   } else if (lane < 32) {
     src.sb = static_cast<const uint8_t*>(a.inter_sf);
-    src.so = (uint32_t)L.rowsrc[32 * w + lane] * (uint32_t)(I / 32);
+    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + lane)] * (uint32_t)(I / 32);
   } else {
     src.sb = static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32);
     src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(I / 32);
@@ -399,7 +441,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   for (int i = 0; i < NG; ++i) {
     const int col = 16 * (2 * i + wn) + lr;
     if (col >= cnt) continue;
-    uint16_t* dst = a.slot + (size_t)a.pool_src[off + col] * H + nbase + 4 * lg;
+    uint16_t* dst = a.slot + (size_t)L.aux[col] * H + nbase + 4 * lg;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const v4f o = acc[rt][i];
@@ -427,7 +469,9 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int n_slabs, Lds&
   __syncthreads();                             // the previous item is done with the LDS
   if (tid < kTok) {
     const int pr = off + (tid < cnt ? tid : cnt - 1);
-    L.rowsrc[tid] = L1 ? a.pool_src[pr] / a.k : pr;
+    const int src_pair = a.pool_src[pr];
+    L.rowsrc[tid] = L1 ? src_pair / a.k : pr;
+    L.aux[tid] = L1 ? __float_as_int(a.w_pool[pr]) : src_pair;
   }
   if (R == 0) {
     if (L1) {

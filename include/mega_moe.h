@@ -70,8 +70,9 @@ typedef enum {
   MEGA_MOE_RECIPE_MXFP4W_B32 = 1
 } mega_moe_recipe;
 
-/* flags: bits 0-1 force the GEMM tile class (0 = choose per expert from its row
-   count, 1 = small-M class only, 2 = large-M class only); other bits must be 0. */
+/* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
+   its row count (currently the large-M class for every expert), 1 = small-M class only,
+   2 = large-M class only); other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u

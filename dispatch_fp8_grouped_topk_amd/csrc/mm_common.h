@@ -20,14 +20,22 @@ constexpr int kLargeRows = 256;       // most pool rows per large-M tile
 constexpr int kLargeMinRows = 1;
 constexpr int kL1SlabCh = 128;        // intermediate channels per L1 workgroup (gate+up = 256 rows)
 constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgroup
+constexpr int kMaxNGClasses = 8;      // large-M tiles: 1..8 column groups of 16 per wave
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
 
-// Rows per large-M tile of an expert with c rows: the rows are split into ceil(c / 256) tiles
-// of equal height, rounded up to a multiple of 16 (the last tile takes the remainder).
-__host__ __device__ inline int large_tile_rows(int c) {
-  const int n = (c + kLargeRows - 1) / kLargeRows;
-  const int per = n ? (c + n - 1) / n : 0;
-  return (per + 15) & ~15;
+// Large-M tiling of an expert with c rows: ceil(c / 256) tiles; the ceil(c / 16) row groups of
+// 16 are dealt out evenly (the first G % n tiles take one extra group), so the tiles' group
+// counts differ by at most one.  Tile i starts at row 16 * (i * (G / n) + min(i, G % n)).
+__host__ __device__ inline int large_tiles(int c) { return (c + kLargeRows - 1) / kLargeRows; }
+__host__ __device__ inline int large_tile_start(int c, int i) {
+  const int n = large_tiles(c), g = (c + 15) / 16;
+  return 16 * (i * (g / n) + (i < g % n ? i : g % n));
+}
+// Column groups per wave of the first (largest) tile of an expert with c > 0 rows: the tile's
+// 16-row groups are shared by two waves.
+__host__ __device__ inline int large_first_ng(int c) {
+  const int n = large_tiles(c), g = (c + 15) / 16;
+  return (g / n + (g % n ? 1 : 0) + 1) / 2;
 }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -58,7 +66,7 @@ struct Args {
   int32_t* pool_src;    // [P]
   float* w_pool;        // [P]
   int2* tiles_s;        // small-M tile list {expert, first pool row}
-  int2* tiles_l;        // large-M tile list
+  int2* tiles_l;        // large-M tile list {expert | rows << 16, first pool row}
   uint8_t* inter_q;     // [P, I]
   void* inter_sf;       // [P, I/128] f32 | [P, I/32] u8
   uint16_t* slot;       // [P, H] bf16, row = pair

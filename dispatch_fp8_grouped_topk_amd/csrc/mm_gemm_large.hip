@@ -460,9 +460,7 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int n_slabs, Lds&
   const int tid = threadIdx.x;
   const int tile = q / n_slabs, slab = q - tile * n_slabs;
   const int2 td = a.tiles_l[tile];
-  const int e = td.x, m0 = td.y;
-  const int c = a.count[e];
-  const int cnt = min(large_tile_rows(c), c - m0);
+  const int e = td.x & 0xFFFF, cnt = td.x >> 16, m0 = td.y;
   const int off = a.offset[e] + m0;
   const int H = a.H, I = a.I;
 

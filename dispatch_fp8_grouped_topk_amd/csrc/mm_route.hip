@@ -109,34 +109,76 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     __syncthreads();
   }
 
-  // 2. offsets (exclusive scan of counts) and the tile lists
-  int carry = 0, carry_s = 0, carry_l = 0;
+  // 2. offsets (exclusive scan of counts) and the tile lists.  Large-M tiles are ordered by the
+  // column-group count of their expert's first tile, largest first (the GEMM kernels deal them
+  // out round-robin, so the costliest items start first and the cheapest fill the tail), and by
+  // expert inside a class, so an expert's tiles stay adjacent.
+  auto large_of = [&](int c) {
+    if (a.tile_mode == 1) return false;
+    if (a.tile_mode == 2) return c > 0;
+    return c > 0 && c >= a.large_min_rows;
+  };
+  __shared__ int s_class_base[kMaxNGClasses + 1];
+  if (tid == 0)
+    for (int g = 0; g <= kMaxNGClasses; ++g) s_class_base[g] = 0;
+  __syncthreads();
+  for (int e0 = 0; e0 < E; e0 += 1024) {       // tiles per class
+    const int e = e0 + tid;
+    const int c = e < E ? s_count[e] : 0;
+    const int ntl = large_of(c) ? large_tiles(c) : 0;
+    const int cls = ntl ? large_first_ng(c) : 0;
+    for (int g = 1; g <= kMaxNGClasses; ++g) {
+      int tot;
+      block_scan_1024(cls == g ? ntl : 0, sh, &tot);
+      if (tid == 0) s_class_base[g] += tot;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {                              // class g starts after all classes above g
+    int run = 0;
+    for (int g = kMaxNGClasses; g >= 1; --g) {
+      const int n = s_class_base[g];
+      s_class_base[g] = run;
+      run += n;
+    }
+    s_class_base[0] = run;                     // total large tiles
+  }
+  __syncthreads();
+  int carry = 0, carry_s = 0;
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + tid;
     const int c = e < E ? s_count[e] : 0;
-    bool large;
-    if (a.tile_mode == 1) large = false;
-    else if (a.tile_mode == 2) large = true;
-    else large = c >= a.large_min_rows;
+    const bool large = large_of(c);
     const int nts = large ? 0 : (c + kSmallRows - 1) / kSmallRows;
-    const int ntl = large ? (c + kLargeRows - 1) / kLargeRows : 0;
-    int tot, tot_s, tot_l;
+    const int ntl = large ? large_tiles(c) : 0;
+    const int cls = ntl ? large_first_ng(c) : 0;
+    int tot, tot_s;
     const int inc = block_scan_1024(c, sh, &tot);
     const int inc_s = block_scan_1024(nts, sh, &tot_s);
-    const int inc_l = block_scan_1024(ntl, sh, &tot_l);
+    int bl = 0;
+    for (int g = 1; g <= kMaxNGClasses; ++g) {
+      int tot_g;
+      const int inc_g = block_scan_1024(cls == g ? ntl : 0, sh, &tot_g);
+      if (cls == g) bl = s_class_base[g] + inc_g - ntl;
+      __syncthreads();
+      if (tid == 0) s_class_base[g] += tot_g;
+      __syncthreads();
+    }
     if (e < E) {
       a.count[e] = c;
       a.offset[e] = carry + inc - c;
       const int bs = carry_s + inc_s - nts;
       for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);
-      const int bl = carry_l + inc_l - ntl;
-      const int per = large_tile_rows(c);
-      for (int i = 0; i < ntl; ++i) a.tiles_l[bl + i] = make_int2(e, i * per);
+      for (int i = 0; i < ntl; ++i) {
+        const int m0 = large_tile_start(c, i);
+        const int m1 = i + 1 < ntl ? large_tile_start(c, i + 1) : c;
+        a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16), m0);
+      }
     }
     carry += tot;
     carry_s += tot_s;
-    carry_l += tot_l;
   }
+  const int carry_l = s_class_base[0];
   if (tid == 0) {
     a.offset[E] = carry;
     a.hdr[kHdrTilesSmall] = carry_s;

@@ -15,9 +15,10 @@
 // Both operands and their scales are staged through LDS with global_load_lds_dwordx4 /
 // global_load_lds_dword (no VGPRs in flight), in a ring of 128-K blocks: three deep for tiles of
 // up to 4 column groups per wave (blocks kb+1 and kb+2 in flight while kb is multiplied), two
-// deep above that, where the larger token tile leaves LDS room for two.  16-byte chunk c of an FP8 row r sits at slot
-// c ^ (r & 7) (FP4 rows of 64 bytes: c ^ ((r >> 1) & 3)), which spreads the operand reads of
-// 16 consecutive rows over all LDS banks.  FP8 recipe: each MFMA covers exactly one 128-K scale
+// deep above that, where the larger token tile leaves LDS room for two.  16-byte chunk c of an
+// FP8 row r sits at slot c ^ ((r >> 1) & 7) (FP4 rows of 64 bytes: c ^ ((r >> 2) & 3)): an
+// operand read serves 16 lanes (16 consecutive rows, one chunk each) per cycle of the 64 LDS
+// banks, and this swizzle puts their chunks in 16 different 16-byte bank groups.  FP8 recipe: each MFMA covers exactly one 128-K scale
 // block and is promoted into the float accumulators with (activation scale x weight scale)
 // one column group later, off the MFMA's critical path.  MXFP4 recipe: the UE8M0 scales go to
 // the MFMA, which accumulates directly.
@@ -95,25 +96,6 @@ __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ v8i read_fp8_rows(const uint8_t* tile, int row, int lg) {
-  const uint8_t* base = tile + row * 128;
-  const int sw = row & 7;
-  const v4i lo = *reinterpret_cast<const v4i*>(base + 16 * (lg ^ sw));
-  const v4i hi = *reinterpret_cast<const v4i*>(base + 16 * ((lg | 4) ^ sw));
-  v8i r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
-__device__ __forceinline__ v8i read_fp4_rows(const uint8_t* tile, int row, int lg) {
-  const v4i lo = *reinterpret_cast<const v4i*>(tile + row * 64 + 16 * (lg ^ ((row >> 1) & 3)));
-  v8i r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-  return r;
-}
-
 // Activation scale word d (0..255; wave d/32, lane d%32 of the scale load) belongs to token row
 // 16 (2i + wn) + lr with wn = d / 128, lr = (d / 8) % 16, i = d % 8, so that the reader (wn, lr)
 // finds the words of its column groups i = 0..7 at 8 consecutive positions, tok_scale_pos.
@@ -175,16 +157,51 @@ __device__ __forceinline__ void wait_block(bool newer, bool tok) {
   }
 }
 
+// LDS operand addressing.  Every row a lane reads has the same residue mod 16 (lr), so the
+// chunk swizzle is the same for all of them and a lane needs two base offsets per tile (the
+// 16-byte chunks of K [16 lg, +16) and [64 + 16 lg, +16) of its first row); the other rows are
+// constant offsets, folded into the ds_read immediates.  L1 weight tiles rt: rows
+// 32 wm + 16 (rt & 1) (+ 128 for the up tiles rt >= 2); L2: rows 64 wm + 16 rt.
+template <bool L1>
+__device__ __forceinline__ constexpr int a_tile_rows(int rt) { return L1 ? (rt >= 2 ? 128 : 0) + 16 * (rt & 1) : 16 * rt; }
+
+__device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* lo, const uint8_t* hi, int off) {
+  const v4i a = *reinterpret_cast<const v4i*>(lo + off);
+  const v4i b = *reinterpret_cast<const v4i*>(hi + off);
+  v8i r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
+  const v4i a = *reinterpret_cast<const v4i*>(lo + off);
+  v8i r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
 // The K loop shared by L1 and L2 for a wave with NG column groups: acc[rt][i] (+)= weight tile
-// rt x column group 2i + wn.  arow[rt]: the lane's LDS row of weight tile rt; wsel[rt]: its
-// FP8 weight-scale block (L.wsc row).
-template <int R, int NG>
-__device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4], const int wsel[4],
-                                       int KB, v4f acc[4][NG], int w, int wn, int lane) {
+// rt x column group 2i + wn.  arow0: the lane's LDS row of weight tile 0; wsel[rt]: the FP8
+// weight-scale block (L.wsc row) of tile rt.
+template <int R, int NG, bool L1>
+__device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const int wsel[4], int KB,
+                                       v4f acc[4][NG], int w, int wn, int lane) {
   constexpr int NS = Ring<NG>::kStages;
   const int lr = lane & 15, lg = lane >> 4;
   const bool tok = w < NG;
   const int tsp = tok_scale_pos(wn, lr);
+  // lane offsets inside a stage's weight and token tiles
+  const int sw7 = (lr >> 1) & 7;
+  const int wlo = R == 0 ? arow0 * 128 + 16 * (lg ^ sw7) : arow0 * 64 + 16 * (lg ^ ((lr >> 2) & 3));
+  const int whi = arow0 * 128 + 16 * ((lg | 4) ^ sw7);
+  const int xrow0 = 16 * wn + lr;
+  const int xlo = xrow0 * 128 + 16 * (lg ^ sw7);
+  const int xhi = xrow0 * 128 + 16 * ((lg | 4) ^ sw7);
+  int swrow[4];                            // MXFP4: scale word index of each weight tile's row
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
   issue_stage<R>(stage_ref<NG>(L.ring, 0), src, 0, w, lane, tok);
   if (NS == 3 && KB > 1) issue_stage<R>(stage_ref<NG>(L.ring, 1), src, 1, w, lane, tok);
   int cur = 0;                           // ring slot of block kb
@@ -199,9 +216,14 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4]
     }
     const StageRef S = stage_ref<NG>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;
+    const uint8_t* xl = S.x + xlo;
+    const uint8_t* xh = S.x + xhi;
     v8i A[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) A[rt] = R == 0 ? read_fp8_rows(S.w, arow[rt], lg) : read_fp4_rows(S.w, arow[rt], lg);
+    for (int rt = 0; rt < 4; ++rt) {
+      if (R == 0) A[rt] = lds_fp8_operand(S.w + wlo, S.w + whi, a_tile_rows<L1>(rt) * 128);
+      else A[rt] = lds_fp4_operand(S.w + wlo, a_tile_rows<L1>(rt) * 64);
+    }
     // activation scale words of column groups 0..NG-1
     uint32_t sw8[8];
     {
@@ -216,12 +238,12 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4]
       float cw[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
-      v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
+      v8i B = lds_fp8_operand(xl, xh, 0);
       v4f p[2][4];
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         v8i Bn;
-        if (i + 1 < NG) Bn = read_fp8_rows(S.x, 16 * (2 * (i + 1) + wn) + lr, lg);
+        if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
         const float sp = i > 0 ? __uint_as_float(sw8[i - 1]) : 0.f;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -246,12 +268,12 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, const int arow[4]
     } else {
       int swv[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[scl_w(arow[rt])] >> (8 * lg)) & 0xFF;
-      v8i B = read_fp8_rows(S.x, 16 * wn + lr, lg);
+      for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[swrow[rt]] >> (8 * lg)) & 0xFF;
+      v8i B = lds_fp8_operand(xl, xh, 0);
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         v8i Bn;
-        if (i + 1 < NG) Bn = read_fp8_rows(S.x, 16 * (2 * (i + 1) + wn) + lr, lg);
+        if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
         const int sx = (sw8[i] >> (8 * lg)) & 0xFF;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_fp4w_fp8(A[rt], B, acc[rt][i], swv[rt], sx);
@@ -266,7 +288,7 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 32 * w + 8 * j + (lane >> 3);
-    s.xo[j] = (uint32_t)rowsrc[r] * row_bytes + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+    s.xo[j] = (uint32_t)rowsrc[r] * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
 }
 
@@ -278,13 +300,13 @@ __device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_byte
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 32 * w + 8 * j + (lane >> 3);
-      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = 32 * w + 16 * j + (lane >> 2);
-      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 3) ^ ((r >> 1) & 3));
+      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
     }
     s.wo[2] = s.wo[3] = 0;
   }
@@ -315,19 +337,16 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
     src.sb = static_cast<const uint8_t*>(a.l1_sf) + (size_t)e * 2 * I * (H / 32);
     src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(H / 32);
   }
-  int arow[4], wsel[4];
+  int wsel[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    arow[rt] = (rt < 2 ? 0 : 128) + 32 * wm + 16 * (rt & 1) + lr;
-    wsel[rt] = rt < 2 ? 0 : 1;
-  }
+  for (int rt = 0; rt < 4; ++rt) wsel[rt] = rt < 2 ? 0 : 1;
 
   v4f acc[4][NG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R, NG>(L, src, arow, wsel, KB, acc, w, wn, lane);
+  k_loop<R, NG, true>(L, src, 32 * wm + lr, wsel, KB, acc, w, wn, lane);
 
   // ---------------- epilogue: SwiGLU, clamp, top-k weight, group amax, scale, E4M3 cast
   // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 16t + 4lg + r of the slab
@@ -420,19 +439,16 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
     src.sb = static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32);
     src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(I / 32);
   }
-  int arow[4], wsel[4];
+  int wsel[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    arow[rt] = 64 * wm + 16 * rt + lr;
-    wsel[rt] = wm >> 1;
-  }
+  for (int rt = 0; rt < 4; ++rt) wsel[rt] = wm >> 1;
 
   v4f acc[4][NG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R, NG>(L, src, arow, wsel, KB, acc, w, wn, lane);
+  k_loop<R, NG, false>(L, src, 64 * wm + lr, wsel, KB, acc, w, wn, lane);
 
   const int nbase = kWRows * slab + 64 * wm;
   if (nbase >= H) return;                        // wave-uniform: H is a multiple of 128

@@ -157,6 +157,13 @@ __device__ __forceinline__ int xcd_logical_id(int hw_id, int grid) {
   return (hw_id & 7) * per + (hw_id >> 3);
 }
 
+// Whether the route kernel can put any expert in the small-M class (known on the host, so the
+// small-M launches are skipped when it cannot).
+inline bool small_class_used(const Args& a) {
+  if (a.max_tiles_s == 0 || a.tile_mode == 2) return false;
+  return a.tile_mode == 1 || a.large_min_rows > 1;
+}
+
 }  // namespace mm
 
 // Host launchers (one per translation unit).

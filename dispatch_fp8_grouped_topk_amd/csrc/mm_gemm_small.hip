@@ -393,7 +393,7 @@ inline int round8(long v) { return (int)((v + 7) / 8 * 8); }
 }  // namespace
 
 hipError_t launch_l1_small(const Args& a, hipStream_t s) {
-  if (a.max_tiles_s == 0 || a.tile_mode == 2) return hipSuccess;
+  if (!small_class_used(a)) return hipSuccess;
   const int grid = round8((long)a.max_tiles_s * (a.I / kL1SlabCh));
   if (a.recipe == 0) hipLaunchKernelGGL(k_l1_small<0>, dim3(grid), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(k_l1_small<1>, dim3(grid), dim3(kThreads), 0, s, a);
@@ -401,7 +401,7 @@ hipError_t launch_l1_small(const Args& a, hipStream_t s) {
 }
 
 hipError_t launch_l2_small(const Args& a, hipStream_t s) {
-  if (a.max_tiles_s == 0 || a.tile_mode == 2) return hipSuccess;
+  if (!small_class_used(a)) return hipSuccess;
   const int grid = round8((long)a.max_tiles_s * ((a.H + kL2SlabRows - 1) / kL2SlabRows));
   if (a.recipe == 0) hipLaunchKernelGGL(k_l2_small<0>, dim3(grid), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(k_l2_small<1>, dim3(grid), dim3(kThreads), 0, s, a);

@@ -77,13 +77,19 @@ struct Lds {
 };
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
 
-// LDS-direct loads: each active lane fetches `size` bytes from its global address into
-// consecutive LDS bytes starting at the wave-uniform `lds` (lane i at lds + size*i).
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// LDS-direct buffer loads: each active lane fetches `size` bytes at byte offset voff + soff of
+// the buffer into consecutive LDS bytes starting at the wave-uniform `lds` (lane i at
+// lds + size*i).  Offsets at or past the buffer's size read zeros instead of faulting.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
-__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
 }
 
 // Workgroup barrier for the K pipeline.  Unlike __syncthreads() it carries no memory fence;
@@ -103,39 +109,49 @@ __device__ __forceinline__ int tok_scale_row(int d) { return 16 * (2 * (d & 7) +
 __device__ __forceinline__ int tok_scale_pos(int wn, int lr) { return 64 * (4 * wn + (lr >> 2)) + 8 * (lr & 3); }
 __device__ __forceinline__ int scl_w(int row) { return 64 * (row >> 5) + 32 + (row & 31); }
 
-// Global sources of one wave's share of a stage, as 32-bit byte offsets from wave-uniform bases
-// (the operand tensors are below 4 GiB; the host routes larger problems to the small class).
+// Global sources of one wave's share of a stage: buffer descriptors and per-lane 32-bit byte
+// offsets (the operand tensors are below 4 GiB; the host routes larger problems to the small
+// class); the K block enters as the scalar offset.
 // FP8 weights: rows 32w + 8j + lane/8 (j < 4); E2M1 weights: rows 32w + 16j + lane/4 (j < 2);
 // tokens: rows 32w + 8j + lane/8 (j < 4); scale word: activation scale word 32w + lane (lanes <
 // 32) or weight row 32w + lane - 32 (lanes >= 32, MXFP4 only).
 struct Src {
-  const uint8_t* wb;
-  const uint8_t* xb;
-  const uint8_t* sb;                          // lane's scale base (token scales or weight scales)
+  rsrc_t wr;                                  // the expert's weight rows
+  rsrc_t xr;                                  // token rows (activations or the intermediate)
+  rsrc_t sr;                                  // activation scales
+  rsrc_t swr;                                 // MXFP4: the expert's weight scales
   uint32_t wo[4];
   uint32_t xo[4];
-  uint32_t so;
+  uint32_t so, swo;
   int wkb;                                    // bytes per K block of a weight row
 };
 
 // tok: this wave's token rows are staged (the first 32 NG rows are; waves past them only fetch
-// weights and scales).  LDS-direct loads per wave and stage: FP8 4 + 4 tok + 1, MXFP4 2 + 4 tok + 1.
+// weights and scales).  LDS-direct loads per wave and stage: FP8 4 + 4 tok + 1, MXFP4 2 + 4 tok + 2.
+// Load j of a wave's share of a stage: weight row chunks first (the longest-latency stream),
+// then token rows, then the scale word.
+template <int R>
+constexpr int kStageLoads = R == 0 ? 9 : 8;
+
+template <int R>
+__device__ __forceinline__ void issue_load(const StageRef& S, const Src& s, int kb, int w, int lane, bool tok, int j) {
+  constexpr int NW = R == 0 ? 4 : 2;
+  if (j < NW) {
+    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
+    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
+  } else if (j < NW + 4) {
+    if (tok) lds_load16(s.xr, s.xo[j - NW], kb * 128, S.x + (32 * w + 8 * (j - NW)) * 128);
+  } else if (j == NW + 4) {
+    if (lane < 32) lds_load4(s.sr, s.so, kb * 4, S.scl + 64 * w);
+  } else if (lane >= 32) {
+    lds_load4(s.swr, s.swo, kb * 4, S.scl + 64 * w);
+  }
+}
+
 template <int R>
 __device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w, int lane, bool tok) {
-  const uint8_t* wk = s.wb + (size_t)kb * s.wkb;
-  const uint8_t* xk = s.xb + (size_t)kb * 128;
-  if (R == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_load16(wk + s.wo[j], S.w + (32 * w + 8 * j) * 128);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) lds_load16(wk + s.wo[j], S.w + (32 * w + 16 * j) * 64);
-  }
-  if (tok) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_load16(xk + s.xo[j], S.x + (32 * w + 8 * j) * 128);
-  }
-  if (R == 1 || lane < 32) lds_load4(s.sb + (size_t)kb * 4 + s.so, S.scl + 64 * w);
+  for (int j = 0; j < kStageLoads<R>; ++j) issue_load<R>(S, s, kb, w, lane, tok, j);
 }
 
 template <int N>
@@ -150,8 +166,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int R, int NS>
 __device__ __forceinline__ void wait_block(bool newer, bool tok) {
   if (NS == 3 && newer) {
-    if (tok) wait_vmcnt<R == 0 ? 9 : 7>();
-    else wait_vmcnt<R == 0 ? 5 : 3>();
+    if (tok) wait_vmcnt<R == 0 ? 9 : 8>();
+    else wait_vmcnt<R == 0 ? 5 : 4>();
   } else {
     wait_vmcnt<0>();
   }
@@ -208,57 +224,80 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   for (int kb = 0; kb < KB; ++kb) {
     wait_block<R, NS>(kb + 1 < KB, tok);
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
-    {
-      const int ahead = kb + NS - 1;
-      int slot = cur + NS - 1;
-      slot = slot >= NS ? slot - NS : slot;
-      if (ahead < KB) issue_stage<R>(stage_ref<NG>(L.ring, slot), src, ahead, w, lane, tok);
-    }
+    // block kb + NS - 1 goes to the slot block kb-1 used.  Its loads are issued behind column
+    // group 0's MFMAs: issued right after the barrier, every wave's loads queue in the address
+    // unit at once and hold the waves back from their first MFMA.
+    const int ahead = kb + NS - 1;
+    int slot = cur + NS - 1;
+    slot = slot >= NS ? slot - NS : slot;
+    const bool fetch = ahead < KB;
+    const StageRef F = stage_ref<NG>(L.ring, slot);
+    constexpr int kPer = kStageLoads<R>;
+    auto fetch_part = [&](int i) {
+      if (fetch) {
+#pragma unroll
+        for (int j = kPer * i; j < kPer * (i + 1) && j < kStageLoads<R>; ++j) issue_load<R>(F, src, ahead, w, lane, tok, j);
+      }
+    };
     const StageRef S = stage_ref<NG>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;
     const uint8_t* xl = S.x + xlo;
     const uint8_t* xh = S.x + xhi;
+    // Column group 0's operands first and alone (10 LDS reads, so the waits before its MFMAs can
+    // count them individually; LDS returns in order); the scales and group 1 follow.
+    v8i B = lds_fp8_operand(xl, xh, 0);
     v8i A[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (R == 0) A[rt] = lds_fp8_operand(S.w + wlo, S.w + whi, a_tile_rows<L1>(rt) * 128);
       else A[rt] = lds_fp4_operand(S.w + wlo, a_tile_rows<L1>(rt) * 64);
     }
-    // activation scale words of column groups 0..NG-1
-    uint32_t sw8[8];
-    {
+    uint32_t sw8[8];                       // activation scale words of column groups 0..NG-1
+    auto read_token_scales = [&]() {
       const v4i lo = *reinterpret_cast<const v4i*>(S.scl + tsp);
       sw8[0] = lo[0]; sw8[1] = lo[1]; sw8[2] = lo[2]; sw8[3] = lo[3];
       if (NG > 4) {
         const v4i hi = *reinterpret_cast<const v4i*>(S.scl + tsp + 4);
         sw8[4] = hi[0]; sw8[5] = hi[1]; sw8[6] = hi[2]; sw8[7] = hi[3];
       }
-    }
+    };
     if (R == 0) {
+      const v8i B1 = NG > 1 ? lds_fp8_operand(xl, xh, 4096) : B;
+      v4f p[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) p[0][rt] = mfma_fp8(A[rt], B);
+      // issue order: group 0's operands and group 1's token tile, then group 0's MFMAs, each
+      // waiting only for its own operands
+      __builtin_amdgcn_sched_group_barrier(0x100, NG > 1 ? 12 : 10, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_part(0);
+      __builtin_amdgcn_sched_barrier(0);
       float cw[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
-      v8i B = lds_fp8_operand(xl, xh, 0);
-      v4f p[2][4];
+      read_token_scales();
+      __builtin_amdgcn_sched_barrier(0);
+      B = B1;
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
+      for (int i = 1; i < NG; ++i) {
         v8i Bn;
         if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
-        const float sp = i > 0 ? __uint_as_float(sw8[i - 1]) : 0.f;
+        const float sp = __uint_as_float(sw8[i - 1]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           p[i & 1][rt] = mfma_fp8(A[rt], B);
-          if (i > 0) acc[rt][i - 1] += p[(i - 1) & 1][rt] * (sp * cw[rt]);
+          acc[rt][i - 1] += p[(i - 1) & 1][rt] * (sp * cw[rt]);
         }
-        if (i > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the next group's LDS reads first
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the next group's LDS reads
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        for (int rt = 0; rt < 4; ++rt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
         }
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_part(i);
         __builtin_amdgcn_sched_barrier(0);
         if (i + 1 < NG) B = Bn;
       }
@@ -269,7 +308,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       int swv[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[swrow[rt]] >> (8 * lg)) & 0xFF;
-      v8i B = lds_fp8_operand(xl, xh, 0);
+      read_token_scales();
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         v8i Bn;
@@ -277,6 +316,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         const int sx = (sw8[i] >> (8 * lg)) & 0xFF;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_fp4w_fp8(A[rt], B, acc[rt][i], swv[rt], sx);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_part(i);
+        __builtin_amdgcn_sched_barrier(0);
         if (i + 1 < NG) B = Bn;
       }
     }
@@ -321,22 +363,19 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   const int H = a.H, I = a.I, KB = H / 128;
 
   Src src;
+  const size_t wrow_bytes = R == 0 ? (size_t)H : (size_t)H / 2;
+  const size_t srow_bytes = R == 0 ? (size_t)KB * 4 : (size_t)H / 32;     // activation scale row
   src.wkb = R == 0 ? 128 : 64;
-  src.wb = a.l1_w + (size_t)e * 2 * I * (R == 0 ? H : H / 2);
-  src.xb = a.x;
+  src.wr = make_rsrc(a.l1_w + (size_t)e * 2 * I * wrow_bytes, 2 * (size_t)I * wrow_bytes);
+  src.xr = make_rsrc(a.x, (size_t)a.T * H);
+  src.sr = make_rsrc(a.x_sf, (size_t)a.T * srow_bytes);
+  src.swr = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R == 1 ? (size_t)e * 2 * I * (H / 32) : 0),
+                      2 * (size_t)I * (H / 32));
   const auto grow = [&](int r) { return r < 128 ? 128 * slab + r : I + 128 * slab + (r - 128); };
-  weight_offsets<R>(src, grow, R == 0 ? H : H / 2, w, lane);
+  weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
   token_offsets(src, L.rowsrc, H, w, lane);
-  if (R == 0) {
-    src.sb = static_cast<const uint8_t*>(a.x_sf);
-    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)(KB * 4);
-  } else if (lane < 32) {
-    src.sb = static_cast<const uint8_t*>(a.x_sf);
-    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + lane)] * (uint32_t)(H / 32);
-  } else {
-    src.sb = static_cast<const uint8_t*>(a.l1_sf) + (size_t)e * 2 * I * (H / 32);
-    src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(H / 32);
-  }
+  src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)srow_bytes;
+  src.swo = R == 1 ? (uint32_t)grow(32 * w + (lane & 31)) * (uint32_t)(H / 32) : 0u;
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = rt < 2 ? 0 : 1;
@@ -422,23 +461,20 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   const int H = a.H, I = a.I, KB = I / 128;
 
   Src src;
+  const size_t wrow_bytes = R == 0 ? (size_t)I : (size_t)I / 2;
+  const size_t srow_bytes = R == 0 ? (size_t)KB * 4 : (size_t)I / 32;     // intermediate scale row
   src.wkb = R == 0 ? 128 : 64;
-  src.wb = a.l2_w + (size_t)e * H * (R == 0 ? I : I / 2);
-  src.xb = a.inter_q;
+  src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
+  src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
+  src.sr = make_rsrc(a.inter_sf, (size_t)a.P * srow_bytes);
+  src.swr = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R == 1 ? (size_t)e * H * (I / 32) : 0),
+                      (size_t)H * (I / 32));
   // tile rows past H (H a multiple of 128 but not of 256) repeat valid rows; their results drop
   const auto grow = [&](int r) { const int g = kWRows * slab + r; return g < H ? g : g - 128; };
-  weight_offsets<R>(src, grow, R == 0 ? I : I / 2, w, lane);
+  weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
   token_offsets(src, L.rowsrc, I, w, lane);
-  if (R == 0) {
-    src.sb = static_cast<const uint8_t*>(a.inter_sf);
-    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)(KB * 4);
-  } else if (lane < 32) {
-    src.sb = static_cast<const uint8_t*>(a.inter_sf);
-    src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + lane)] * (uint32_t)(I / 32);
-  } else {
-    src.sb = static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32);
-    src.so = (uint32_t)grow(32 * w + lane - 32) * (uint32_t)(I / 32);
-  }
+  src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)srow_bytes;
+  src.swo = R == 1 ? (uint32_t)grow(32 * w + (lane & 31)) * (uint32_t)(I / 32) : 0u;
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = wm >> 1;

@@ -12,10 +12,10 @@
 // column groups g = 2i + (w >> 2) of the tile.  The kernels are instantiated per number of
 // column groups per wave (1..8), so a ragged tile costs at most one padded group per wave.
 //
-// Both operands and their scales are staged through LDS with global_load_lds_dwordx4 /
-// global_load_lds_dword (no VGPRs in flight), in a ring of 128-K blocks: three deep for tiles of
-// up to 4 column groups per wave (blocks kb+1 and kb+2 in flight while kb is multiplied), two
-// deep above that, where the larger token tile leaves LDS room for two.  16-byte chunk c of an
+// Both operands and their scales are staged through LDS with LDS-direct buffer loads (no
+// VGPRs in flight), in a ring of 128-K blocks as deep as LDS allows for the tile shape (four
+// blocks for one column group per wave, two for the largest FP8 tiles): while block kb is
+// multiplied, blocks kb+1 .. kb+depth-1 are in flight.  16-byte chunk c of an
 // FP8 row r sits at slot c ^ ((r >> 1) & 7) (FP4 rows of 64 bytes: c ^ ((r >> 2) & 3)): an
 // operand read serves 16 lanes (16 consecutive rows, one chunk each) per cycle of the 64 LDS
 // banks, and this swizzle puts their chunks in 16 different 16-byte bank groups.  FP8 recipe: each MFMA covers exactly one 128-K scale
@@ -41,20 +41,24 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTok = kLargeRows;              // pool rows per tile (256)
 constexpr int kWRows = 256;                   // weight rows per tile
 
-// Ring geometry for NG column groups per wave: a stage holds the 256 weight rows, the first
-// 32 NG token rows (128 bytes each, E2M1 weights use the first 64 of a weight row) and 512
+// Ring geometry for recipe R and NG column groups per wave: a stage holds the 256 weight rows
+// (128 bytes of E4M3 or 64 of E2M1 each), the first 32 NG token rows (128 bytes each) and 512
 // scale words: per wave w, words [64w, 64w+32) are activation scale words in the order
 // (wn, lr, i) of the readers (see tok_scale_row) and words [64w+32, 64w+64) the MXFP4 scale
-// words (4 x UE8M0) of weight rows 32w...
-template <int NG>
+// words (4 x UE8M0) of weight rows 32w...  The ring takes as many stages (2 to 4) as fit in the
+// LDS left beside the per-tile arrays.
+constexpr int kRingBudget = 160 * 1024 - 7 * 1024;
+
+template <int R, int NG>
 struct Ring {
+  static constexpr int kWBytes = kWRows * (R == 0 ? 128 : 64);
   static constexpr int kXRows = 32 * NG;
-  static constexpr int kStageBytes = kWRows * 128 + kXRows * 128 + 2048;
-  static constexpr int kStages = NG <= 4 ? 3 : 2;
+  static constexpr int kStageBytes = kWBytes + kXRows * 128 + 2048;
+  static constexpr int kFit = kRingBudget / kStageBytes;
+  static constexpr int kStages = kFit > 4 ? 4 : kFit;
+  static_assert(kStages >= 2, "two stages must fit");
 };
-constexpr int kRingBytes = Ring<4>::kStages * Ring<4>::kStageBytes > Ring<8>::kStages * Ring<8>::kStageBytes
-                               ? Ring<4>::kStages * Ring<4>::kStageBytes
-                               : Ring<8>::kStages * Ring<8>::kStageBytes;
+constexpr int kRingBytes = kRingBudget;
 
 struct StageRef {
   uint8_t* w;
@@ -62,10 +66,11 @@ struct StageRef {
   uint32_t* scl;
 };
 
-template <int NG>
+template <int R, int NG>
 __device__ __forceinline__ StageRef stage_ref(uint8_t* ring, int s) {
-  uint8_t* b = ring + s * Ring<NG>::kStageBytes;
-  return StageRef{b, b + kWRows * 128, reinterpret_cast<uint32_t*>(b + kWRows * 128 + Ring<NG>::kXRows * 128)};
+  using G = Ring<R, NG>;
+  uint8_t* b = ring + s * G::kStageBytes;
+  return StageRef{b, b + G::kWBytes, reinterpret_cast<uint32_t*>(b + G::kWBytes + G::kXRows * 128)};
 }
 
 struct Lds {
@@ -161,16 +166,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until this wave's loads of block kb have landed: with a three-deep ring the loads of
-// block kb+1 (if any) may stay in flight.
+// Wait until this wave's loads of block kb have landed; the loads of the `newer` blocks issued
+// after it (0 .. NS-2) may stay in flight.
+template <int R, int N>
+__device__ __forceinline__ void wait_newer(bool tok) {
+  if (tok) wait_vmcnt<N * (R == 0 ? 9 : 8)>();
+  else wait_vmcnt<N * (R == 0 ? 5 : 4)>();
+}
 template <int R, int NS>
-__device__ __forceinline__ void wait_block(bool newer, bool tok) {
-  if (NS == 3 && newer) {
-    if (tok) wait_vmcnt<R == 0 ? 9 : 8>();
-    else wait_vmcnt<R == 0 ? 5 : 4>();
-  } else {
-    wait_vmcnt<0>();
-  }
+__device__ __forceinline__ void wait_block(int newer, bool tok) {
+  if (NS >= 4 && newer >= 2) wait_newer<R, 2>(tok);
+  else if (NS >= 3 && newer >= 1) wait_newer<R, 1>(tok);
+  else wait_vmcnt<0>();
 }
 
 // LDS operand addressing.  Every row a lane reads has the same residue mod 16 (lr), so the
@@ -204,7 +211,7 @@ __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
 template <int R, int NG, bool L1>
 __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const int wsel[4], int KB,
                                        v4f acc[4][NG], int w, int wn, int lane) {
-  constexpr int NS = Ring<NG>::kStages;
+  constexpr int NS = Ring<R, NG>::kStages;
   const int lr = lane & 15, lg = lane >> 4;
   const bool tok = w < NG;
   const int tsp = tok_scale_pos(wn, lr);
@@ -218,11 +225,12 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   int swrow[4];                            // MXFP4: scale word index of each weight tile's row
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
-  issue_stage<R>(stage_ref<NG>(L.ring, 0), src, 0, w, lane, tok);
-  if (NS == 3 && KB > 1) issue_stage<R>(stage_ref<NG>(L.ring, 1), src, 1, w, lane, tok);
+#pragma unroll
+  for (int b = 0; b < NS - 1; ++b)
+    if (b < KB) issue_stage<R>(stage_ref<R, NG>(L.ring, b), src, b, w, lane, tok);
   int cur = 0;                           // ring slot of block kb
   for (int kb = 0; kb < KB; ++kb) {
-    wait_block<R, NS>(kb + 1 < KB, tok);
+    wait_block<R, NS>(min(NS - 2, KB - 1 - kb), tok);
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
     // block kb + NS - 1 goes to the slot block kb-1 used.  Its loads are issued behind column
     // group 0's MFMAs: issued right after the barrier, every wave's loads queue in the address
@@ -231,7 +239,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     int slot = cur + NS - 1;
     slot = slot >= NS ? slot - NS : slot;
     const bool fetch = ahead < KB;
-    const StageRef F = stage_ref<NG>(L.ring, slot);
+    const StageRef F = stage_ref<R, NG>(L.ring, slot);
     constexpr int kPer = kStageLoads<R>;
     auto fetch_part = [&](int i) {
       if (fetch) {
@@ -239,7 +247,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         for (int j = kPer * i; j < kPer * (i + 1) && j < kStageLoads<R>; ++j) issue_load<R>(F, src, ahead, w, lane, tok, j);
       }
     };
-    const StageRef S = stage_ref<NG>(L.ring, cur);
+    const StageRef S = stage_ref<R, NG>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;
     const uint8_t* xl = S.x + xlo;
     const uint8_t* xh = S.x + xhi;

@@ -214,35 +214,54 @@ hipError_t launch_route(const Args& a, hipStream_t s) {
 // ---------------------------------------------------------------------------------- combine
 // grid (ceil(H / 2048), min(T, 65535)); each thread owns 8 consecutive columns of a token
 // and strides over tokens.
+// One thread per (token, 8 output columns), grid-stride over all of them.  The slot rows of a
+// token are fetched 8 top-k slots at a time (their pair_pos words first, then every active
+// row's 16 bytes), so each thread keeps several loads in flight; the sum is still taken in
+// ascending slot order.
 __global__ __launch_bounds__(256) void k_combine(Args a) {
-  const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (n0 >= a.H) return;
-  for (int t = blockIdx.y; t < a.T; t += gridDim.y) {
-  float acc[8];
+  const int cpt = a.H / 8;                       // 8-column chunks per token
+  const long total = (long)a.T * cpt;
+  for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long)gridDim.x * 256) {
+    const int t = (int)(idx / cpt);
+    const int n0 = (int)(idx - (long)t * cpt) * 8;
+    float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < a.k; ++j) {
-    const int pair = t * a.k + j;
-    if (a.pair_pos[pair] < 0) continue;          // masked or invalid slot
-    const v4i v = *reinterpret_cast<const v4i*>(a.slot + (size_t)pair * a.H + n0);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+      int pp[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = (uint32_t)v[i];
-      acc[2 * i] += __uint_as_float(w << 16);
-      acc[2 * i + 1] += __uint_as_float(w & 0xFFFF0000u);
+      for (int jj = 0; jj < 8; ++jj) pp[jj] = j0 + jj < a.k ? a.pair_pos[(size_t)t * a.k + j0 + jj] : -1;
+      v4i v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        v[jj] = v4i{0, 0, 0, 0};
+        if (pp[jj] >= 0)                         // masked or invalid slots contribute nothing
+          v[jj] = *reinterpret_cast<const v4i*>(a.slot + ((size_t)t * a.k + j0 + jj) * a.H + n0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (pp[jj] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = (uint32_t)v[jj][i];
+          acc[2 * i] += __uint_as_float(w << 16);
+          acc[2 * i + 1] += __uint_as_float(w & 0xFFFF0000u);
+        }
+      }
     }
-  }
-  v4i o;
+    v4i o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (int)(bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16));
-  *reinterpret_cast<v4i*>(a.y + (size_t)t * a.H + n0) = o;
+    for (int i = 0; i < 4; ++i) o[i] = (int)(bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16));
+    *reinterpret_cast<v4i*>(a.y + (size_t)t * a.H + n0) = o;
   }
 }
 
 hipError_t launch_combine(const Args& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  dim3 grid((a.H + 2047) / 2048, a.T < 65535 ? a.T : 65535);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, a);
+  const long total = (long)a.T * (a.H / 8);
+  long blocks = (total + 255) / 256;
+  blocks = blocks < 8192 ? blocks : 8192;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

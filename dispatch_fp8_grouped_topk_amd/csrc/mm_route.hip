@@ -47,31 +47,42 @@ __global__ __launch_bounds__(kRouteBlock) void k_route_count(Args a) {
   }
 }
 
-// Inclusive scan of one int per thread over a 1024-thread workgroup; returns the inclusive
-// value and writes the workgroup total to *total.
-__device__ int block_scan_1024(int v, int* sh, int* total) {
+// Inclusive scans of N ints per thread at once over a 1024-thread workgroup (one round of
+// barriers for all N); totals of each written to total[0..N).  sh must hold 32 * N ints.
+template <int N>
+__device__ void block_scan_1024_n(int v[N], int* sh, int total[N]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  // wave-level inclusive scan
+#pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int o = __shfl_up(v[n], d, 64);
+      if (lane >= d) v[n] += o;
+    }
   }
-  if (lane == 63) sh[w] = v;
+  if (lane == 63)
+#pragma unroll
+    for (int n = 0; n < N; ++n) sh[n * 32 + w] = v[n];
   __syncthreads();
   if (w == 0) {
-    int s = lane < 16 ? sh[lane] : 0;
-    for (int d = 1; d < 16; d <<= 1) {
-      int o = __shfl_up(s, d, 64);
-      if (lane >= d) s += o;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      int x = lane < 16 ? sh[n * 32 + lane] : 0;
+      for (int d = 1; d < 16; d <<= 1) {
+        const int o = __shfl_up(x, d, 64);
+        if (lane >= d) x += o;
+      }
+      if (lane < 16) sh[n * 32 + 16 + lane] = x;
     }
-    if (lane < 16) sh[16 + lane] = s;
   }
   __syncthreads();
-  int base = w > 0 ? sh[16 + w - 1] : 0;
-  *total = sh[16 + 15];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    v[n] += w > 0 ? sh[n * 32 + 16 + w - 1] : 0;
+    total[n] = sh[n * 32 + 31];
+  }
   __syncthreads();
-  return v + base;
 }
 
 // ---------------------------------------------------------------------------------- scan
@@ -80,7 +91,7 @@ __device__ int block_scan_1024(int v, int* sh, int* total) {
 __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
   __shared__ int s_count[kMaxExperts];
   __shared__ int part[4][256];
-  __shared__ int sh[64];
+  __shared__ int sh[32 * (kMaxNGClasses + 2)];
   const int tid = threadIdx.x;
   const int E = a.E, NB = a.NB;
 
@@ -127,11 +138,12 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     const int c = e < E ? s_count[e] : 0;
     const int ntl = large_of(c) ? large_tiles(c) : 0;
     const int cls = ntl ? large_first_ng(c) : 0;
-    for (int g = 1; g <= kMaxNGClasses; ++g) {
-      int tot;
-      block_scan_1024(cls == g ? ntl : 0, sh, &tot);
-      if (tid == 0) s_class_base[g] += tot;
-    }
+    int v[kMaxNGClasses], tot[kMaxNGClasses];
+#pragma unroll
+    for (int g = 0; g < kMaxNGClasses; ++g) v[g] = cls == g + 1 ? ntl : 0;
+    block_scan_1024_n<kMaxNGClasses>(v, sh, tot);
+    if (tid == 0)
+      for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tot[g - 1];
   }
   __syncthreads();
   if (tid == 0) {                              // class g starts after all classes above g
@@ -152,18 +164,19 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     const int nts = large ? 0 : (c + kSmallRows - 1) / kSmallRows;
     const int ntl = large ? large_tiles(c) : 0;
     const int cls = ntl ? large_first_ng(c) : 0;
-    int tot, tot_s;
-    const int inc = block_scan_1024(c, sh, &tot);
-    const int inc_s = block_scan_1024(nts, sh, &tot_s);
+    int v[kMaxNGClasses + 2], tv[kMaxNGClasses + 2];
+    v[0] = c;
+    v[1] = nts;
+#pragma unroll
+    for (int g = 0; g < kMaxNGClasses; ++g) v[2 + g] = cls == g + 1 ? ntl : 0;
+    block_scan_1024_n<kMaxNGClasses + 2>(v, sh, tv);
+    const int inc = v[0], tot = tv[0], inc_s = v[1], tot_s = tv[1];
     int bl = 0;
-    for (int g = 1; g <= kMaxNGClasses; ++g) {
-      int tot_g;
-      const int inc_g = block_scan_1024(cls == g ? ntl : 0, sh, &tot_g);
-      if (cls == g) bl = s_class_base[g] + inc_g - ntl;
-      __syncthreads();
-      if (tid == 0) s_class_base[g] += tot_g;
-      __syncthreads();
-    }
+    if (cls > 0) bl = s_class_base[cls] + v[1 + cls] - ntl;
+    __syncthreads();
+    if (tid == 0)
+      for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tv[1 + g];
+    __syncthreads();
     if (e < E) {
       a.count[e] = c;
       a.offset[e] = carry + inc - c;

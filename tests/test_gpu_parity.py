@@ -52,6 +52,9 @@ SMALL = {
     "mxfp4": synth.Spec(40, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=107, weight_set=107),
     "mxfp4_multi_tile": synth.Spec(200, 512, 256, 3, 2, recipe=1, seed=108, weight_set=108),
     "mxfp4_clamp": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.05, seed=109, weight_set=109),
+    # more than 16384 pairs: dispatch runs 1024 pairs per workgroup; skewed so that experts
+    # fill every large-M column-group class
+    "wide_dispatch": synth.Spec(2100, 512, 256, 64, 8, routing="zipf", seed=115, weight_set=115),
 }
 
 

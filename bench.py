@@ -35,10 +35,16 @@ TRAFFIC_FILE = os.path.join("profiles", "hbm_traffic.json")
 
 
 def kernel_source_sha256():
+    """sha256 of the kernel sources with comments and whitespace removed (so editing a comment
+    does not disown counter data taken on the same machine code)."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -240,6 +240,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     slot = slot >= NS ? slot - NS : slot;
     const bool fetch = ahead < KB;
     const StageRef F = stage_ref<R, NG>(L.ring, slot);
+    // fetch_part(i) issues the stage loads due after column group i: all of them after group
+    // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
+    // the group loop's schedule; removing them measured slower.)
     constexpr int kPer = kStageLoads<R>;
     auto fetch_part = [&](int i) {
       if (fetch) {

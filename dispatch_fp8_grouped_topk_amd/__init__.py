@@ -208,14 +208,11 @@ def mega_moe_workspace_views(problem: Problem, workspace) -> dict:
     T, H, I, E, k = (problem.num_tokens, problem.hidden, problem.intermediate,
                      problem.num_experts, problem.topk)
     P = T * k
-    g = 128 if problem.recipe == RECIPE_FP8_B128 else 32
 
     def view(addr, nbytes, dtype, shape):
         off = addr - base
         return raw[off:off + nbytes].view(dtype).reshape(shape)
 
-    sf_dtype = torch.float32 if problem.recipe == RECIPE_FP8_B128 else torch.uint8
-    sf_size = 4 if problem.recipe == RECIPE_FP8_B128 else 1
     return dict(
         expert_count=view(v.expert_count, 4 * E, torch.int32, (E,)),
         expert_offset=view(v.expert_offset, 4 * (E + 1), torch.int32, (E + 1,)),
@@ -223,7 +220,9 @@ def mega_moe_workspace_views(problem: Problem, workspace) -> dict:
         pair_pos=view(v.pair_pos, 4 * P, torch.int32, (P,)),
         num_invalid=view(v.num_invalid, 4, torch.int32, (1,)),
         inter_q=view(v.inter_q, P * I, torch.uint8, (P, I)),
-        inter_sf=view(v.inter_sf, P * (I // g) * sf_size, sf_dtype, (P, I // g)),
+        inter_sf=(view(v.inter_sf, P * (I // 128) * 4, torch.float32, (I // 128, P)).t()
+                  if problem.recipe == RECIPE_FP8_B128 else
+                  view(v.inter_sf, P * (I // 32), torch.uint8, (I // 128, P, 4)).permute(1, 0, 2).reshape(P, I // 32)),
         slot=view(v.slot, P * H * 2, torch.int16, (P, H)),
     )
 

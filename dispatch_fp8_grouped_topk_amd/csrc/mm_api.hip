@@ -16,8 +16,8 @@
 namespace {
 
 struct Layout {
-  size_t hdr, count, offset, blk, blk_inv, pair_pos, pool_src, w_pool, tiles_s, tiles_l, inter_q,
-      inter_sf, slot, total;
+  size_t hdr, count, offset, blk, blk_inv, pair_pos, pool_src, w_pool, tiles_s, tiles_l, x_sf_pool,
+      inter_q, inter_sf, slot, total;
   int P, NB, max_tiles_s, max_tiles_l;
 };
 
@@ -60,6 +60,7 @@ Layout make_layout(const mega_moe_problem* p) {
   L.w_pool = take(P * 4);
   L.tiles_s = take(ts * 8);
   L.tiles_l = take(tl * 8);
+  L.x_sf_pool = take(P * (H / 128) * 4);
   L.inter_q = take(P * I);
   L.inter_sf = take(p->recipe == MEGA_MOE_RECIPE_FP8_B128 ? P * (I / 128) * 4 : P * (I / 32));
   L.slot = take(P * H * 2);
@@ -183,6 +184,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.w_pool = reinterpret_cast<float*>(w + L.w_pool);
   a.tiles_s = reinterpret_cast<int2*>(w + L.tiles_s);
   a.tiles_l = reinterpret_cast<int2*>(w + L.tiles_l);
+  a.x_sf_pool = w + L.x_sf_pool;
   a.inter_q = w + L.inter_q;
   a.inter_sf = w + L.inter_sf;
   a.slot = reinterpret_cast<uint16_t*>(w + L.slot);

@@ -67,8 +67,9 @@ struct Args {
   float* w_pool;        // [P]
   int2* tiles_s;        // small-M tile list {expert, first pool row}
   int2* tiles_l;        // large-M tile list {expert | rows << 16, first pool row}
+  void* x_sf_pool;      // [H/128][P] words: the x_sf word of each K block of each pool row
   uint8_t* inter_q;     // [P, I]
-  void* inter_sf;       // [P, I/128] f32 | [P, I/32] u8
+  void* inter_sf;       // [I/128][P] words: f32 | 4 x UE8M0 (K-major, like x_sf_pool)
   uint16_t* slot;       // [P, H] bf16, row = pair
   // sizes
   int T, H, I, E, k, P, NB;

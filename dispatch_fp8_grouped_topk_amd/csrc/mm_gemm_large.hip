@@ -23,9 +23,10 @@
 // one column group later, off the MFMA's critical path.  MXFP4 recipe: the UE8M0 scales go to
 // the MFMA, which accumulates directly.
 //
-// The grid is persistent: each workgroup walks the (tile, slab) items with a stride of the
-// grid, and the 32 workgroups resident on one XCD take consecutive items, i.e. the slabs of
-// the same one or two token tiles, which then share those token rows in the XCD's L2.
+// The grid is persistent: the workgroups walk the (tile, slab) items in rounds, half of each
+// round from the costly end of the item list and half from the cheap end (see k_large), and
+// the 32 workgroups resident on one XCD take consecutive items, i.e. the slabs of the same one
+// or two token tiles, which then share those token rows in the XCD's L2.
 //
 // The epilogues are those of the small-M kernels: fused SwiGLU / clamp / top-k weight / group
 // amax / scale / E4M3 cast after L1 (design page section 10.1), BF16 slot rows after L2
@@ -43,10 +44,10 @@ constexpr int kWRows = 256;                   // weight rows per tile
 
 // Ring geometry for recipe R and NG column groups per wave: a stage holds the 256 weight rows
 // (128 bytes of E4M3 or 64 of E2M1 each), the first 32 NG token rows (128 bytes each) and 512
-// scale words: per wave w, words [64w, 64w+32) are activation scale words in the order
-// (wn, lr, i) of the readers (see tok_scale_row) and words [64w+32, 64w+64) the MXFP4 scale
-// words (4 x UE8M0) of weight rows 32w...  The ring takes as many stages (2 to 4) as fit in the
-// LDS left beside the per-tile arrays.
+// scale words: words [0, 256) are activation scale words in the order (wn, lr, i) of the
+// readers (see tok_scale_row), words [256, 512) the MXFP4 scale words (4 x UE8M0) of weight
+// rows 0..255.  The ring takes as many stages (2 to 4) as fit in the LDS left beside the
+// per-tile arrays.
 constexpr int kRingBudget = 160 * 1024 - 7 * 1024;
 
 template <int R, int NG>
@@ -107,56 +108,62 @@ __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Activation scale word d (0..255; wave d/32, lane d%32 of the scale load) belongs to token row
+// Activation scale word d (0..255; wave d/64, lane d%64 of the scale load) belongs to token row
 // 16 (2i + wn) + lr with wn = d / 128, lr = (d / 8) % 16, i = d % 8, so that the reader (wn, lr)
 // finds the words of its column groups i = 0..7 at 8 consecutive positions, tok_scale_pos.
 __device__ __forceinline__ int tok_scale_row(int d) { return 16 * (2 * (d & 7) + (d >> 7)) + ((d >> 3) & 15); }
-__device__ __forceinline__ int tok_scale_pos(int wn, int lr) { return 64 * (4 * wn + (lr >> 2)) + 8 * (lr & 3); }
-__device__ __forceinline__ int scl_w(int row) { return 64 * (row >> 5) + 32 + (row & 31); }
+__device__ __forceinline__ int tok_scale_pos(int wn, int lr) { return 128 * wn + 8 * lr; }
+__device__ __forceinline__ int scl_w(int row) { return 256 + row; }
 
 // Global sources of one wave's share of a stage: buffer descriptors and per-lane 32-bit byte
 // offsets (the operand tensors are below 4 GiB; the host routes larger problems to the small
-// class); the K block enters as the scalar offset.
-// FP8 weights: rows 32w + 8j + lane/8 (j < 4); E2M1 weights: rows 32w + 16j + lane/4 (j < 2);
-// tokens: rows 32w + 8j + lane/8 (j < 4); scale word: activation scale word 32w + lane (lanes <
-// 32) or weight row 32w + lane - 32 (lanes >= 32, MXFP4 only).
+// class); the K block enters as the scalar offset.  Every wave issues the same loads per stage,
+// with no branch, so that a K step is one basic block and the scheduling fences below hold:
+//   weights: FP8 rows 32w + 8j + lane/8 (j < 4); E2M1 rows 32w + 16j + lane/4 (j < 2);
+//   tokens:  ceil(NG/2) blocks of 8 rows, rows 8 token_block(w, j) + lane/8;
+//   scales:  one word per lane: waves 0-3 the activation scale word 64w + lane, from the
+//            K-major pool-order scale array (one K block of the tile's rows is one contiguous
+//            kilobyte: a gather of one word per row costs the address unit about a lane a
+//            cycle), waves 4-7 the MXFP4 scale word of weight row 64(w-4) + lane (FP8: a
+//            filler, the first word of the array, into words nobody reads).
 struct Src {
   rsrc_t wr;                                  // the expert's weight rows
   rsrc_t xr;                                  // token rows (activations or the intermediate)
-  rsrc_t sr;                                  // activation scales
-  rsrc_t swr;                                 // MXFP4: the expert's weight scales
+  rsrc_t cr;                                  // this wave's scale source
   uint32_t wo[4];
   uint32_t xo[4];
-  uint32_t so, swo;
+  uint32_t co;
   int wkb;                                    // bytes per K block of a weight row
+  int ckb;                                    // bytes per K block of this wave's scale source
 };
 
-// tok: this wave's token rows are staged (the first 32 NG rows are; waves past them only fetch
-// weights and scales).  LDS-direct loads per wave and stage: FP8 4 + 4 tok + 1, MXFP4 2 + 4 tok + 2.
-// Load j of a wave's share of a stage: weight row chunks first (the longest-latency stream),
-// then token rows, then the scale word.
 template <int R>
-constexpr int kStageLoads = R == 0 ? 9 : 8;
+constexpr int kWeightLoads = R == 0 ? 4 : 2;
+template <int NG>
+constexpr int kTokenLoads = (NG + 1) / 2;
+template <int R, int NG>
+constexpr int kStageLoads = kWeightLoads<R> + kTokenLoads<NG> + 1;
 
-template <int R>
-__device__ __forceinline__ void issue_load(const StageRef& S, const Src& s, int kb, int w, int lane, bool tok, int j) {
-  constexpr int NW = R == 0 ? 4 : 2;
-  if (j < NW) {
-    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
-    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
-  } else if (j < NW + 4) {
-    if (tok) lds_load16(s.xr, s.xo[j - NW], kb * 128, S.x + (32 * w + 8 * (j - NW)) * 128);
-  } else if (j == NW + 4) {
-    if (lane < 32) lds_load4(s.sr, s.so, kb * 4, S.scl + 64 * w);
-  } else if (lane >= 32) {
-    lds_load4(s.swr, s.swo, kb * 4, S.scl + 64 * w);
-  }
+// 8-row token block of load j of wave w: blocks w + 8j cover the 4 NG blocks of the tile; for
+// odd NG, waves 4-7 have no block left in their last load and fetch wave w-4's again (the same
+// bytes to the same place).
+template <int NG>
+__device__ __forceinline__ int token_block(int w, int j) {
+  const int b = w + 8 * j;
+  return (NG & 1) && j == kTokenLoads<NG> - 1 && w >= 4 ? b - 4 : b;
 }
 
-template <int R>
-__device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w, int lane, bool tok) {
+template <int R, int NG>
+__device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w) {
 #pragma unroll
-  for (int j = 0; j < kStageLoads<R>; ++j) issue_load<R>(S, s, kb, w, lane, tok, j);
+  for (int j = 0; j < kWeightLoads<R>; ++j) {
+    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
+    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
+  }
+#pragma unroll
+  for (int j = 0; j < kTokenLoads<NG>; ++j)
+    lds_load16(s.xr, s.xo[j], kb * 128, S.x + token_block<NG>(w, j) * 8 * 128);
+  lds_load4(s.cr, s.co, kb * s.ckb, S.scl + 64 * w);
 }
 
 template <int N>
@@ -166,17 +173,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until this wave's loads of block kb have landed; the loads of the `newer` blocks issued
-// after it (0 .. NS-2) may stay in flight.
-template <int R, int N>
-__device__ __forceinline__ void wait_newer(bool tok) {
-  if (tok) wait_vmcnt<N * (R == 0 ? 9 : 8)>();
-  else wait_vmcnt<N * (R == 0 ? 5 : 4)>();
-}
-template <int R, int NS>
-__device__ __forceinline__ void wait_block(int newer, bool tok) {
-  if (NS >= 4 && newer >= 2) wait_newer<R, 2>(tok);
-  else if (NS >= 3 && newer >= 1) wait_newer<R, 1>(tok);
+// Wait until this wave's loads of block kb have landed while the loads of the `newer` stages
+// issued after it (0 .. NS-2) may stay in flight.
+template <int R, int NG, int NS>
+__device__ __forceinline__ void wait_block(int newer) {
+  if (NS >= 4 && newer >= 2) wait_vmcnt<2 * kStageLoads<R, NG>>();
+  else if (NS >= 3 && newer >= 1) wait_vmcnt<kStageLoads<R, NG>>();
   else wait_vmcnt<0>();
 }
 
@@ -213,7 +215,6 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
                                        v4f acc[4][NG], int w, int wn, int lane) {
   constexpr int NS = Ring<R, NG>::kStages;
   const int lr = lane & 15, lg = lane >> 4;
-  const bool tok = w < NG;
   const int tsp = tok_scale_pos(wn, lr);
   // lane offsets inside a stage's weight and token tiles
   const int sw7 = (lr >> 1) & 7;
@@ -227,28 +228,27 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
 #pragma unroll
   for (int b = 0; b < NS - 1; ++b)
-    if (b < KB) issue_stage<R>(stage_ref<R, NG>(L.ring, b), src, b, w, lane, tok);
+    if (b < KB) issue_stage<R, NG>(stage_ref<R, NG>(L.ring, b), src, b, w);
+  // Every K step issues one stage: block kb + NS - 1, or past the end a copy of block KB - 1
+  // (into the slot of a retired block, never read), so that the issue has no branch and the
+  // number of stages in flight behind block kb is always min(NS - 1, KB) - 1.
+  const int newer = min(NS - 2, KB - 1);
   int cur = 0;                           // ring slot of block kb
   for (int kb = 0; kb < KB; ++kb) {
-    wait_block<R, NS>(min(NS - 2, KB - 1 - kb), tok);
+    wait_block<R, NG, NS>(newer);
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
     // block kb + NS - 1 goes to the slot block kb-1 used.  Its loads are issued behind column
     // group 0's MFMAs: issued right after the barrier, every wave's loads queue in the address
     // unit at once and hold the waves back from their first MFMA.
-    const int ahead = kb + NS - 1;
+    const int ahead = min(kb + NS - 1, KB - 1);
     int slot = cur + NS - 1;
     slot = slot >= NS ? slot - NS : slot;
-    const bool fetch = ahead < KB;
     const StageRef F = stage_ref<R, NG>(L.ring, slot);
     // fetch_part(i) issues the stage loads due after column group i: all of them after group
     // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
-    // the group loop's schedule; removing them measured slower.)
-    constexpr int kPer = kStageLoads<R>;
+    // the group loop's schedule.)
     auto fetch_part = [&](int i) {
-      if (fetch) {
-#pragma unroll
-        for (int j = kPer * i; j < kPer * (i + 1) && j < kStageLoads<R>; ++j) issue_load<R>(F, src, ahead, w, lane, tok, j);
-      }
+      if (i == 0) issue_stage<R, NG>(F, src, ahead, w);
     };
     const StageRef S = stage_ref<R, NG>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;
@@ -336,12 +336,29 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   }
 }
 
-// Per-lane global offsets of one wave's share of the token rows (tile rows 32w + 8j + lane/8).
-__device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, int w, int lane) {
+// Per-lane global offsets of one wave's share of the token rows (tile rows
+// 8 token_block(w, j) + lane/8) and of its scale word.  sf_pool: the K-major activation scales
+// ([KB][P] words; the tile's rows are pool rows off .. off + cnt - 1, padding rows repeat the
+// last); w_sf: the MXFP4 weight scale rows, grow(r) maps a tile row to the weight row within
+// the expert.
+template <int R, int NG, class F>
+__device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, rsrc_t sf_pool,
+                                              int P, int off, int cnt, rsrc_t w_sf, F grow,
+                                              uint32_t wsrow_bytes, int w, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < kTokenLoads<NG>; ++j) {
+    const int r = 8 * token_block<NG>(w, j) + (lane >> 3);
     s.xo[j] = (uint32_t)rowsrc[r] * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+  }
+  const int d = 64 * (w & 3) + lane;
+  const bool wscale = R == 1 && w >= 4;
+  s.cr = wscale ? w_sf : sf_pool;
+  s.ckb = wscale ? 4 : 4 * P;
+  if (w < 4) {
+    const int r = tok_scale_row(d);
+    s.co = 4u * (uint32_t)(off + (r < cnt ? r : cnt - 1));
+  } else {
+    s.co = R == 1 ? (uint32_t)grow(d) * wsrow_bytes : 0u;   // FP8: one word, read by every lane
   }
 }
 
@@ -375,18 +392,15 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 
   Src src;
   const size_t wrow_bytes = R == 0 ? (size_t)H : (size_t)H / 2;
-  const size_t srow_bytes = R == 0 ? (size_t)KB * 4 : (size_t)H / 32;     // activation scale row
   src.wkb = R == 0 ? 128 : 64;
   src.wr = make_rsrc(a.l1_w + (size_t)e * 2 * I * wrow_bytes, 2 * (size_t)I * wrow_bytes);
   src.xr = make_rsrc(a.x, (size_t)a.T * H);
-  src.sr = make_rsrc(a.x_sf, (size_t)a.T * srow_bytes);
-  src.swr = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R == 1 ? (size_t)e * 2 * I * (H / 32) : 0),
-                      2 * (size_t)I * (H / 32));
+  const rsrc_t sf_pool = make_rsrc(a.x_sf_pool, (size_t)KB * a.P * 4);
+  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R == 1 ? (size_t)e * 2 * I * (H / 32) : 0),
+                                2 * (size_t)I * (H / 32));
   const auto grow = [&](int r) { return r < 128 ? 128 * slab + r : I + 128 * slab + (r - 128); };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
-  token_offsets(src, L.rowsrc, H, w, lane);
-  src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)srow_bytes;
-  src.swo = R == 1 ? (uint32_t)grow(32 * w + (lane & 31)) * (uint32_t)(H / 32) : 0u;
+  token_offsets<R, NG>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, H / 32, w, lane);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = rt < 2 ? 0 : 1;
@@ -438,7 +452,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
       }
       if (valid && lg == 0)
-        static_cast<uint8_t*>(a.inter_sf)[(size_t)(off + col) * (I / 32) + 4 * slab + wm] = (uint8_t)code;
+        static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + wm] = (uint8_t)code;
     }
   }
   if (R == 0) {
@@ -458,7 +472,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
         if (valid)
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
       }
-      if (valid && wm == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)(off + col) * (I / 128) + slab] = sf;
+      if (valid && wm == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)slab * a.P + off + col] = sf;
     }
   }
 }
@@ -473,19 +487,16 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
 
   Src src;
   const size_t wrow_bytes = R == 0 ? (size_t)I : (size_t)I / 2;
-  const size_t srow_bytes = R == 0 ? (size_t)KB * 4 : (size_t)I / 32;     // intermediate scale row
   src.wkb = R == 0 ? 128 : 64;
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
-  src.sr = make_rsrc(a.inter_sf, (size_t)a.P * srow_bytes);
-  src.swr = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R == 1 ? (size_t)e * H * (I / 32) : 0),
-                      (size_t)H * (I / 32));
+  const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
+  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R == 1 ? (size_t)e * H * (I / 32) : 0),
+                                (size_t)H * (I / 32));
   // tile rows past H (H a multiple of 128 but not of 256) repeat valid rows; their results drop
   const auto grow = [&](int r) { const int g = kWRows * slab + r; return g < H ? g : g - 128; };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
-  token_offsets(src, L.rowsrc, I, w, lane);
-  src.so = (uint32_t)L.rowsrc[tok_scale_row(32 * w + (lane & 31))] * (uint32_t)srow_bytes;
-  src.swo = R == 1 ? (uint32_t)grow(32 * w + (lane & 31)) * (uint32_t)(I / 32) : 0u;
+  token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, I / 32, w, lane);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = wm >> 1;
@@ -574,9 +585,25 @@ __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   __shared__ __attribute__((aligned(1024))) Lds L;
   const int n_slabs = L1 ? a.I / kL1SlabCh : (a.H + kWRows - 1) / kWRows;
   const int n_items = a.hdr[kHdrTilesLarge] * n_slabs;
-  const int G = gridDim.x, per = G >> 3;
+  // The item list runs from the costliest tiles (most column groups: MFMA-bound) to the
+  // cheapest (few tokens per weight byte: HBM-bound).  Each round, half the grid (four XCDs)
+  // takes the next items from the front of the list and the other half the next ones from the
+  // back, and the halves swap every round, so both kinds run side by side (the weight stream of
+  // the cheap items overlaps the MFMA work of the costly ones) and every workgroup alternates
+  // between them.  Slot `mine` is XCD-major, so each XCD still takes consecutive items.
+  const int G = gridDim.x, per = G >> 3, half = G >> 1;
   const int mine = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  for (int base = 0; base + mine < n_items; base += G) run_item<R, L1>(a, base + mine, n_slabs, L);
+  const int n_front = (n_items + 1) >> 1, n_back = n_items - n_front;
+  const bool first_half = mine < half;
+  const int k0 = first_half ? mine : mine - half;
+  for (int r = 0; r * half < n_front; ++r) {
+    const int k = r * half + k0;
+    if (first_half == ((r & 1) == 0)) {
+      if (k < n_front) run_item<R, L1>(a, k, n_slabs, L);
+    } else if (k < n_back) {
+      run_item<R, L1>(a, n_items - 1 - k, n_slabs, L);
+    }
+  }
 }
 
 template <bool L1>

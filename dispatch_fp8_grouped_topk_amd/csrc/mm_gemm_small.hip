@@ -197,7 +197,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
       }
       if (valid && lg == 0)
-        static_cast<uint8_t*>(a.inter_sf)[(size_t)(off + col) * (I / 32) + 4 * slab + w] = (uint8_t)code;
+        static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + w] = (uint8_t)code;
     }
   }
   if (R == 0) {
@@ -217,7 +217,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
         if (valid)
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
       }
-      if (valid && w == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)(off + col) * (I / 128) + slab] = sf;
+      if (valid && w == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)slab * a.P + off + col] = sf;
     }
   }
 }
@@ -257,7 +257,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
     const float* isf = static_cast<const float*>(a.inter_sf);
     for (int i = tid; i < 64 * KB; i += kThreads) {
       const int row = i / KB;
-      sfa[i] = isf[(size_t)(off + (row < cnt ? row : cnt - 1)) * KB + i % KB];
+      sfa[i] = isf[(size_t)(i % KB) * a.P + off + (row < cnt ? row : cnt - 1)];
     }
   } else {
     const int G4 = I / 128;                                    // words of 4 UE8M0 codes per row
@@ -265,7 +265,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
     uint32_t* sfx = reinterpret_cast<uint32_t*>(s_scale);
     for (int i = tid; i < 64 * G4; i += kThreads) {
       const int row = i / G4;
-      sfx[i] = isf[(size_t)(off + (row < cnt ? row : cnt - 1)) * G4 + i % G4];
+      sfx[i] = isf[(size_t)(i % G4) * a.P + off + (row < cnt ? row : cnt - 1)];
     }
   }
   __syncthreads();

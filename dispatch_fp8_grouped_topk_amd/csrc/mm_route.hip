@@ -216,11 +216,40 @@ __global__ __launch_bounds__(kRouteBlock) void k_route_scatter(Args a) {
   a.w_pool[pos] = a.topk_w[pair];
 }
 
+// ------------------------------------------------------------------------ pool-order scales
+// x_sf_pool[kb][r] = the x_sf word of K block kb of pool row r's token (an f32 scale, or the
+// four UE8M0 codes of the block), K-major, so that the large-M L1 kernel reads one K block's
+// scales of a tile's rows from one contiguous kilobyte instead of one scattered word per row.
+// grid (ceil(P / 256), ceil(KB / 8)); a thread copies 8 K blocks of one pool row.
+__global__ __launch_bounds__(256) void k_pool_scales(Args a) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.offset[a.E]) return;
+  const int KB = a.H / 128, kb0 = blockIdx.y * 8;
+  const int t = a.pool_src[r] / a.k;
+  const uint32_t* src = static_cast<const uint32_t*>(a.x_sf) + (size_t)t * KB + kb0;
+  uint32_t* dst = static_cast<uint32_t*>(a.x_sf_pool) + (size_t)kb0 * a.P + r;
+  uint32_t v[8];
+  if ((KB & 3) == 0) {                         // rows of whole 16-byte chunks
+    const uint4 lo = *reinterpret_cast<const uint4*>(src);
+    const uint4 hi = kb0 + 4 < KB ? *reinterpret_cast<const uint4*>(src + 4) : lo;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = kb0 + j < KB ? src[j] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (kb0 + j < KB) dst[(size_t)j * a.P] = v[j];
+}
+
 hipError_t launch_route(const Args& a, hipStream_t s) {
   if (a.P == 0) return hipSuccess;
   hipLaunchKernelGGL(k_route_count, dim3(a.NB), dim3(kRouteBlock), (size_t)a.E * sizeof(int), s, a);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(k_route_scatter, dim3(a.NB), dim3(kRouteBlock), 0, s, a);
+  if (a.max_tiles_l > 0 && a.tile_mode != 1)
+    hipLaunchKernelGGL(k_pool_scales, dim3((a.P + 255) / 256, (a.H / 128 + 7) / 8), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -108,7 +108,8 @@ typedef struct {
   const int32_t* pair_pos;       /* [T*k] pair -> pool row, -1 when masked or invalid */
   const int32_t* num_invalid;    /* [1]   ids >= E seen in topk_idx */
   const uint8_t* inter_q;        /* [T*k, I] E4M3 intermediate per pool row */
-  const void* inter_sf;          /* [T*k, I/128] f32 | [T*k, I/32] u8 */
+  const void* inter_sf;          /* K-major: [I/128, T*k] f32 | [I/128, T*k, 4] u8 (the four
+                                    per-32 codes of one 128 block); pool row r, block b at b*T*k+r */
   const uint16_t* slot;          /* [T*k, H] BF16 L2 output per pair (t*k+j order) */
 } mega_moe_views;
 

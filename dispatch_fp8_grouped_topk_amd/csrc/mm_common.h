@@ -66,7 +66,7 @@ struct Args {
   int32_t* pool_src;    // [P]
   float* w_pool;        // [P]
   int2* tiles_s;        // small-M tile list {expert, first pool row}
-  int2* tiles_l;        // large-M tile list {expert | rows << 16, first pool row}
+  int2* tiles_l;        // large-M tile list {expert | rows << 16, first pool row (absolute)}
   void* x_sf_pool;      // [H/128][P] words: the x_sf word of each K block of each pool row
   uint8_t* inter_q;     // [P, I]
   void* inter_sf;       // [I/128][P] words: f32 | 4 x UE8M0 (K-major, like x_sf_pool)

@@ -48,7 +48,7 @@ constexpr int kWRows = 256;                   // weight rows per tile
 // readers (see tok_scale_row), words [256, 512) the MXFP4 scale words (4 x UE8M0) of weight
 // rows 0..255.  The ring takes as many stages (2 to 4) as fit in the LDS left beside the
 // per-tile arrays.
-constexpr int kRingBudget = 160 * 1024 - 7 * 1024;
+constexpr int kRingBudget = 160 * 1024 - 7 * 1024 - 256;
 
 template <int R, int NG>
 struct Ring {
@@ -80,6 +80,7 @@ struct Lds {
   int aux[kTok];                              // L1: top-k weight (f32 bits) / L2: slot row, per tile row
   float red[4][kTok];                         // FP8 L1 epilogue: amax per (row group, token)
   float wsc[2][kMaxKBlocks];                  // FP8 recipe: weight-block scales per K block
+  int2 td_next;                               // tile-list entry of the workgroup's next item
 };
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
 
@@ -104,6 +105,15 @@ __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, int soff, voi
 // the empty asm statements stop the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are complete, but its
+// global stores may still be in flight (__syncthreads() would wait for those too; vmcnt counts
+// stores).  The LDS-direct loads are waited for explicitly (wait_vmcnt) where they matter.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -334,6 +344,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       }
     }
   }
+  // the copies issued past the last block land in retired slots; let them land before the
+  // item ends, so none can reach the LDS once the next item (or kernel) has laid it out anew
+  wait_vmcnt<0>();
 }
 
 // Per-lane global offsets of one wave's share of the token rows (tile rows
@@ -493,8 +506,15 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
   const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R == 1 ? (size_t)e * H * (I / 32) : 0),
                                 (size_t)H * (I / 32));
-  // tile rows past H (H a multiple of 128 but not of 256) repeat valid rows; their results drop
-  const auto grow = [&](int r) { const int g = kWRows * slab + r; return g < H ? g : g - 128; };
+  // Tile row 64 wm + 16 rt + m holds output column 64 wm + 16 (m / 4) + 4 rt + m % 4 of the
+  // slab: the lane holding rows 4 lg .. 4 lg + 3 of the four tiles then holds 16 consecutive
+  // output columns of its token, stored as two 16-byte pieces.  Columns past H (H a multiple
+  // of 128 but not of 256) repeat valid rows; their results drop.
+  const auto grow = [&](int r) {
+    const int m = r & 15, rt = (r >> 4) & 3;
+    const int g = kWRows * slab + (r & ~63) + 16 * (m >> 2) + 4 * rt + (m & 3);
+    return g < H ? g : g - 128;
+  };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
   token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, I / 32, w, lane);
   int wsel[4];
@@ -511,34 +531,40 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   const int nbase = kWRows * slab + 64 * wm;
   if (nbase >= H) return;                        // wave-uniform: H is a multiple of 128
   // ---------------- epilogue: BF16 rows into the pair-ordered slot buffer
+  // acc[rt][i][j] is output column nbase + 16 lg + 4 rt + j of tile row 16 (2i + wn) + lr
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int col = 16 * (2 * i + wn) + lr;
     if (col >= cnt) continue;
-    uint16_t* dst = a.slot + (size_t)L.aux[col] * H + nbase + 4 * lg;
+    uint16_t* dst = a.slot + (size_t)L.aux[col] * H + nbase + 16 * lg;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const v4f o = acc[rt][i];
-      uint2 pk;
-      pk.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
-      pk.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
-      *reinterpret_cast<uint2*>(dst + 16 * rt) = pk;
+    for (int h = 0; h < 2; ++h) {
+      const v4f o0 = acc[2 * h][i], o1 = acc[2 * h + 1][i];
+      uint4 pk;
+      pk.x = bf16_rne(o0[0]) | (bf16_rne(o0[1]) << 16);
+      pk.y = bf16_rne(o0[2]) | (bf16_rne(o0[3]) << 16);
+      pk.z = bf16_rne(o1[0]) | (bf16_rne(o1[1]) << 16);
+      pk.w = bf16_rne(o1[2]) | (bf16_rne(o1[3]) << 16);
+      *reinterpret_cast<uint4*>(dst + 8 * h) = pk;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------ kernels
 // Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
+// The item's tile-list entry is in L.td_next (fetched during the previous item); q_next is the
+// workgroup's next item (-1: none), whose entry this item fetches in turn.
 template <int R, bool L1>
-__device__ __forceinline__ void run_item(const Args& a, int q, int n_slabs, Lds& L) {
+__device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n_slabs, Lds& L) {
   const int tid = threadIdx.x;
-  const int tile = q / n_slabs, slab = q - tile * n_slabs;
-  const int2 td = a.tiles_l[tile];
-  const int e = td.x & 0xFFFF, cnt = td.x >> 16, m0 = td.y;
-  const int off = a.offset[e] + m0;
+  const int slab = q % n_slabs;
   const int H = a.H, I = a.I;
 
-  __syncthreads();                             // the previous item is done with the LDS
+  // the previous item is done with the LDS (its LDS-direct loads were waited for at the end of
+  // its K loop; its output stores need not have completed)
+  lds_barrier();
+  const int2 td = L.td_next;
+  const int e = td.x & 0xFFFF, cnt = td.x >> 16, off = td.y;
   if (tid < kTok) {
     const int pr = off + (tid < cnt ? tid : cnt - 1);
     const int src_pair = a.pool_src[pr];
@@ -563,7 +589,12 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int n_slabs, Lds&
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // every wave has read td: fetch the next item's entry straight into LDS (two lanes of wave 0);
+  // it is older than all of this item's stage loads, so the K loop's first wait covers it
+  if (q_next >= 0 && tid < 2)
+    lds_load4(make_rsrc(a.tiles_l, (size_t)a.max_tiles_l * 8), (uint32_t)(q_next / n_slabs) * 8u + 4u * tid, 0,
+              &L.td_next);
 
   const int nw = ((cnt + 15) / 16 + 1) / 2;    // column groups per wave
   switch (nw) {
@@ -596,13 +627,19 @@ __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   const int n_front = (n_items + 1) >> 1, n_back = n_items - n_front;
   const bool first_half = mine < half;
   const int k0 = first_half ? mine : mine - half;
-  for (int r = 0; r * half < n_front; ++r) {
+  // item of round r, -1 if none (once a round has none, no later round has one)
+  const auto item = [&](int r) {
     const int k = r * half + k0;
-    if (first_half == ((r & 1) == 0)) {
-      if (k < n_front) run_item<R, L1>(a, k, n_slabs, L);
-    } else if (k < n_back) {
-      run_item<R, L1>(a, n_items - 1 - k, n_slabs, L);
-    }
+    if (first_half == ((r & 1) == 0)) return k < n_front ? k : -1;
+    return k < n_back ? n_items - 1 - k : -1;
+  };
+  const int rounds = (n_front + half - 1) / half;
+  int q = rounds > 0 ? item(0) : -1;
+  if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[q / n_slabs];
+  for (int r = 0; q >= 0; ++r) {
+    const int q_next = r + 1 < rounds ? item(r + 1) : -1;
+    run_item<R, L1>(a, q, q_next, n_slabs, L);
+    q = q_next;
   }
 }
 

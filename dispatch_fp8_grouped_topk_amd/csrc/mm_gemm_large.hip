@@ -411,7 +411,14 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   const rsrc_t sf_pool = make_rsrc(a.x_sf_pool, (size_t)KB * a.P * 4);
   const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R == 1 ? (size_t)e * 2 * I * (H / 32) : 0),
                                 2 * (size_t)I * (H / 32));
-  const auto grow = [&](int r) { return r < 128 ? 128 * slab + r : I + 128 * slab + (r - 128); };
+  // Gate tile row 32 wm + 16 t + m (and the up tile row 128 further on) holds channel
+  // 32 wm + 8 (m / 4) + 4 t + m % 4 of the slab: the lane holding rows 4 lg .. 4 lg + 3 of both
+  // gate tiles then holds 8 consecutive channels of its token, stored as one 8-byte piece.
+  const auto grow = [&](int r) {
+    const int q = r & 127, m = q & 15;
+    const int c = (q & ~31) + 8 * (m >> 2) + 4 * ((q >> 4) & 1) + (m & 3);
+    return (r < 128 ? 0 : I) + 128 * slab + c;
+  };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
   token_offsets<R, NG>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, H / 32, w, lane);
   int wsel[4];
@@ -426,7 +433,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   k_loop<R, NG, true>(L, src, 32 * wm + lr, wsel, KB, acc, w, wn, lane);
 
   // ---------------- epilogue: SwiGLU, clamp, top-k weight, group amax, scale, E4M3 cast
-  // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 16t + 4lg + r of the slab
+  // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 8lg + 4t + r of the slab
   // for tile row 16(2i + wn) + lr.
   const bool do_clamp = a.clamp > 0.f;
   float v[NG][2][4];
@@ -455,15 +462,15 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
       const uint32_t code = ue8m0_for_amax(am);
       const int ex = 127 - (int)code;
       const bool valid = col < cnt;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t q = 0;
-        if (am > 0.f)
-          q = pack_fp8x4(clamp448(ldexpf(v[i][t][0], ex)), clamp448(ldexpf(v[i][t][1], ex)),
-                         clamp448(ldexpf(v[i][t][2], ex)), clamp448(ldexpf(v[i][t][3], ex)));
-        if (valid)
-          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
+      uint2 q = make_uint2(0u, 0u);
+      if (am > 0.f) {
+        q.x = pack_fp8x4(clamp448(ldexpf(v[i][0][0], ex)), clamp448(ldexpf(v[i][0][1], ex)),
+                         clamp448(ldexpf(v[i][0][2], ex)), clamp448(ldexpf(v[i][0][3], ex)));
+        q.y = pack_fp8x4(clamp448(ldexpf(v[i][1][0], ex)), clamp448(ldexpf(v[i][1][1], ex)),
+                         clamp448(ldexpf(v[i][1][2], ex)), clamp448(ldexpf(v[i][1][3], ex)));
       }
+      if (valid)
+        *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
       if (valid && lg == 0)
         static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + wm] = (uint8_t)code;
     }
@@ -476,15 +483,15 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
       const float amax = fmaxf(fmaxf(L.red[0][col], L.red[1][col]), fmaxf(L.red[2][col], L.red[3][col]));
       const float sf = amax / 448.0f;
       const bool valid = col < cnt;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t q = 0;
-        if (sf > 0.f)
-          q = pack_fp8x4(clamp448(v[i][t][0] / sf), clamp448(v[i][t][1] / sf),
-                         clamp448(v[i][t][2] / sf), clamp448(v[i][t][3] / sf));
-        if (valid)
-          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 16 * t + 4 * lg) = q;
+      uint2 q = make_uint2(0u, 0u);
+      if (sf > 0.f) {
+        q.x = pack_fp8x4(clamp448(v[i][0][0] / sf), clamp448(v[i][0][1] / sf),
+                         clamp448(v[i][0][2] / sf), clamp448(v[i][0][3] / sf));
+        q.y = pack_fp8x4(clamp448(v[i][1][0] / sf), clamp448(v[i][1][1] / sf),
+                         clamp448(v[i][1][2] / sf), clamp448(v[i][1][3] / sf));
       }
+      if (valid)
+        *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
       if (valid && wm == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)slab * a.P + off + col] = sf;
     }
   }

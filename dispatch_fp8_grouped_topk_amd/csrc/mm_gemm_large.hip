@@ -149,6 +149,7 @@ struct Src {
 
 template <int R>
 constexpr int kWeightLoads = R == 0 ? 4 : 2;
+constexpr int kSpreadGroups = 3;              // column groups the stage loads are spread over
 template <int NG>
 constexpr int kTokenLoads = (NG + 1) / 2;
 template <int R, int NG>
@@ -163,17 +164,33 @@ __device__ __forceinline__ int token_block(int w, int j) {
   return (NG & 1) && j == kTokenLoads<NG> - 1 && w >= 4 ? b - 4 : b;
 }
 
+// Load j of a wave's share of a stage: weights, then token blocks, then the scale word.
+template <int R, int NG>
+__device__ __forceinline__ void issue_load(const StageRef& S, const Src& s, int kb, int w, int j) {
+  constexpr int NW = kWeightLoads<R>, NT = kTokenLoads<NG>;
+  if (j < NW) {
+    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
+    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
+  } else if (j < NW + NT) {
+    lds_load16(s.xr, s.xo[j - NW], kb * 128, S.x + token_block<NG>(w, j - NW) * 8 * 128);
+  } else {
+    lds_load4(s.cr, s.co, kb * s.ckb, S.scl + 64 * w);
+  }
+}
+
 template <int R, int NG>
 __device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w) {
 #pragma unroll
-  for (int j = 0; j < kWeightLoads<R>; ++j) {
-    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
-    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
-  }
-#pragma unroll
-  for (int j = 0; j < kTokenLoads<NG>; ++j)
-    lds_load16(s.xr, s.xo[j], kb * 128, S.x + token_block<NG>(w, j) * 8 * 128);
-  lds_load4(s.cr, s.co, kb * s.ckb, S.scl + 64 * w);
+  for (int j = 0; j < kStageLoads<R, NG>; ++j) issue_load<R, NG>(S, s, kb, w, j);
+}
+
+// The stage loads of a K step go out behind the MFMAs of its column groups: after group i,
+// loads [stage_split(i), stage_split(i + 1)).  Issued all at once, a wave stalls in the address
+// unit until the queue has room for them; spread out, the queue drains between groups.
+template <int R, int NG>
+__device__ __forceinline__ constexpr int stage_split(int i) {
+  constexpr int C = kStageLoads<R, NG>, G = NG < kSpreadGroups ? NG : kSpreadGroups;
+  return i >= G ? C : (C * i + G - 1) / G;
 }
 
 template <int N>
@@ -258,7 +275,8 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
     // the group loop's schedule.)
     auto fetch_part = [&](int i) {
-      if (i == 0) issue_stage<R, NG>(F, src, ahead, w);
+#pragma unroll
+      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG>(F, src, ahead, w, j);
     };
     const StageRef S = stage_ref<R, NG>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;

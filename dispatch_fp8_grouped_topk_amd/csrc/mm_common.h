@@ -99,6 +99,18 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// silu(g) = g / (1 + exp(-g)) with the hardware exp and reciprocal instructions (float32 to a
+// few ulp); where exp(-g) overflows (g below about -88) the result is -0, as in the exact form.
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// E4M3 codes of four values divided by sf = amax / 448 (amax > 0): multiplied by m = 448 / amax,
+// one IEEE division per group instead of one per value (the product is within about one ulp of
+// the quotient before the E4M3 rounding), or divided by sf where m overflows (amax < ~2^-119).
+__device__ __forceinline__ uint32_t e4m3_scaled4(float a, float b, float c, float d, float m, float sf) {
+  if (__builtin_isfinite(m)) return pack_fp8x4(clamp448(a * m), clamp448(b * m), clamp448(c * m), clamp448(d * m));
+  return pack_fp8x4(clamp448(a / sf), clamp448(b / sf), clamp448(c / sf), clamp448(d / sf));
+}
+
 // UE8M0 code of the smallest power of two 2^E with amax / 2^E <= 448:
 // r = amax / 448 (IEEE division), E = ceil(log2 r) read off r's exponent and mantissa bits,
 // code = clamp(E + 127, 0, 254); amax == 0 -> 0.

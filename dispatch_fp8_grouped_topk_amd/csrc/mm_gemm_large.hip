@@ -465,7 +465,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[t][i][r], u = acc[2 + t][i][r];
-        float sv = g / (1.0f + expf(-g)) * u;
+        float sv = silu_f32(g) * u;
         if (do_clamp) sv = fminf(fmaxf(sv, -a.clamp), a.clamp);
         const float x = sv * wt;
         v[i][t][r] = x;
@@ -499,14 +499,12 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
     for (int i = 0; i < NG; ++i) {
       const int col = 16 * (2 * i + wn) + lr;
       const float amax = fmaxf(fmaxf(L.red[0][col], L.red[1][col]), fmaxf(L.red[2][col], L.red[3][col]));
-      const float sf = amax / 448.0f;
+      const float sf = amax / 448.0f, m = 448.0f / amax;
       const bool valid = col < cnt;
       uint2 q = make_uint2(0u, 0u);
       if (sf > 0.f) {
-        q.x = pack_fp8x4(clamp448(v[i][0][0] / sf), clamp448(v[i][0][1] / sf),
-                         clamp448(v[i][0][2] / sf), clamp448(v[i][0][3] / sf));
-        q.y = pack_fp8x4(clamp448(v[i][1][0] / sf), clamp448(v[i][1][1] / sf),
-                         clamp448(v[i][1][2] / sf), clamp448(v[i][1][3] / sf));
+        q.x = e4m3_scaled4(v[i][0][0], v[i][0][1], v[i][0][2], v[i][0][3], m, sf);
+        q.y = e4m3_scaled4(v[i][1][0], v[i][1][1], v[i][1][2], v[i][1][3], m, sf);
       }
       if (valid)
         *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
@@ -576,13 +574,31 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
 }
 
 // ------------------------------------------------------------------------------------ kernels
+// Item numbering: the tile list is cut into bands of kBand consecutive tiles (the last band may
+// be shorter), and a band's items run slab-major: item (band b, slab s, j-th tile of the band).
+// 32 consecutive items, which one XCD's workgroups take together, then cover 32 / kBand slabs
+// of kBand tiles, so an expert's weight slab is fetched into that XCD's L2 once for up to
+// kBand of its tiles, and each tile's rows once for 32 / kBand slabs.
+constexpr int kBand = 4;
+
+struct ItemPos {
+  int tile, slab;
+};
+__device__ __forceinline__ ItemPos item_pos(int q, int n_slabs, int n_tiles) {
+  const int per_band = kBand * n_slabs;
+  const int b = q / per_band, r = q - b * per_band;
+  const int in_band = min(kBand, n_tiles - b * kBand);
+  const int s = r / in_band;
+  return ItemPos{b * kBand + (r - s * in_band), s};
+}
+
 // Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
 // The item's tile-list entry is in L.td_next (fetched during the previous item); q_next is the
 // workgroup's next item (-1: none), whose entry this item fetches in turn.
 template <int R, bool L1>
-__device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n_slabs, Lds& L) {
+__device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n_slabs, int n_tiles, Lds& L) {
   const int tid = threadIdx.x;
-  const int slab = q % n_slabs;
+  const int slab = item_pos(q, n_slabs, n_tiles).slab;
   const int H = a.H, I = a.I;
 
   // the previous item is done with the LDS (its LDS-direct loads were waited for at the end of
@@ -618,7 +634,8 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   // every wave has read td: fetch the next item's entry straight into LDS (two lanes of wave 0);
   // it is older than all of this item's stage loads, so the K loop's first wait covers it
   if (q_next >= 0 && tid < 2)
-    lds_load4(make_rsrc(a.tiles_l, (size_t)a.max_tiles_l * 8), (uint32_t)(q_next / n_slabs) * 8u + 4u * tid, 0,
+    lds_load4(make_rsrc(a.tiles_l, (size_t)a.max_tiles_l * 8),
+              (uint32_t)item_pos(q_next, n_slabs, n_tiles).tile * 8u + 4u * tid, 0,
               &L.td_next);
 
   const int nw = ((cnt + 15) / 16 + 1) / 2;    // column groups per wave
@@ -634,13 +651,14 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   }
 }
 
-// Persistent item loop: item q = (tile q / n_slabs, slab q % n_slabs).  Round r gives XCD x
+// Persistent item loop over the items numbered as above.  Round r gives XCD x
 // (hardware workgroup id mod 8) the items r*G + x*(G/8) + j for its workgroups j.
 template <int R, bool L1>
 __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   __shared__ __attribute__((aligned(1024))) Lds L;
   const int n_slabs = L1 ? a.I / kL1SlabCh : (a.H + kWRows - 1) / kWRows;
-  const int n_items = a.hdr[kHdrTilesLarge] * n_slabs;
+  const int n_tiles = a.hdr[kHdrTilesLarge];
+  const int n_items = n_tiles * n_slabs;
   // The item list runs from the costliest tiles (most column groups: MFMA-bound) to the
   // cheapest (few tokens per weight byte: HBM-bound).  Each round, half the grid (four XCDs)
   // takes the next items from the front of the list and the other half the next ones from the
@@ -660,10 +678,10 @@ __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   };
   const int rounds = (n_front + half - 1) / half;
   int q = rounds > 0 ? item(0) : -1;
-  if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[q / n_slabs];
+  if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[item_pos(q, n_slabs, n_tiles).tile];
   for (int r = 0; q >= 0; ++r) {
     const int q_next = r + 1 < rounds ? item(r + 1) : -1;
-    run_item<R, L1>(a, q, q_next, n_slabs, L);
+    run_item<R, L1>(a, q, q_next, n_slabs, n_tiles, L);
     q = q_next;
   }
 }

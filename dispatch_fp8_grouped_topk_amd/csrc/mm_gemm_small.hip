@@ -172,7 +172,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[i][s][r], u = acc[2 + i][s][r];
-        float sv = g / (1.0f + expf(-g)) * u;
+        float sv = silu_f32(g) * u;
         if (do_clamp) sv = fminf(fmaxf(sv, -a.clamp), a.clamp);
         const float x = sv * wt;
         v[s][i][r] = x;
@@ -206,14 +206,12 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
     for (int s = 0; s < NSUB; ++s) {
       const int col = 16 * s + lr;
       const float amax = fmaxf(fmaxf(s_red[col], s_red[64 + col]), fmaxf(s_red[128 + col], s_red[192 + col]));
-      const float sf = amax / 448.0f;
+      const float sf = amax / 448.0f, m = 448.0f / amax;
       const bool valid = col < cnt;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint32_t q = 0;
-        if (sf > 0.f)
-          q = pack_fp8x4(clamp448(v[s][i][0] / sf), clamp448(v[s][i][1] / sf),
-                         clamp448(v[s][i][2] / sf), clamp448(v[s][i][3] / sf));
+        if (sf > 0.f) q = e4m3_scaled4(v[s][i][0], v[s][i][1], v[s][i][2], v[s][i][3], m, sf);
         if (valid)
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
       }

@@ -42,22 +42,28 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTok = kLargeRows;              // pool rows per tile (256)
 constexpr int kWRows = 256;                   // weight rows per tile
 
-// Ring geometry for recipe R and NG column groups per wave: a stage holds the 256 weight rows
-// (128 bytes of E4M3 or 64 of E2M1 each), the first 32 NG token rows (128 bytes each) and 512
-// scale words: words [0, 256) are activation scale words in the order (wn, lr, i) of the
-// readers (see tok_scale_row), words [256, 512) the MXFP4 scale words (4 x UE8M0) of weight
-// rows 0..255.  The ring takes as many stages (2 to 4) as fit in the LDS left beside the
-// per-tile arrays.
-constexpr int kRingBudget = 160 * 1024 - 7 * 1024 - 256;
+// Ring geometry for recipe R and NG column groups per wave.  A stage of block kb has a weight
+// part (the 256 weight rows: 128 bytes of E4M3 or 64 of E2M1 each) and a token part (the first
+// 32 NG token rows, 128 bytes each, and 512 scale words: words [0, 256) are activation scale
+// words in the order (wn, lr, i) of the readers (see tok_scale_row), words [256, 512) the MXFP4
+// scale words (4 x UE8M0) of weight rows 0..255).  The weight parts and the token parts sit in
+// two rings.  Where three or four whole stages fit in the LDS left beside the per-tile arrays,
+// both rings take that depth; where only two would, the weight ring (streamed from HBM, the
+// loads with the longest latency) takes three and the token ring (rows shared by the slabs of
+// a tile, mostly served by L2) two, if that fits.
+constexpr int kRingBudget = 160 * 1024 - 3 * 1024 - 256;
 
 template <int R, int NG>
 struct Ring {
   static constexpr int kWBytes = kWRows * (R == 0 ? 128 : 64);
   static constexpr int kXRows = 32 * NG;
-  static constexpr int kStageBytes = kWBytes + kXRows * 128 + 2048;
-  static constexpr int kFit = kRingBudget / kStageBytes;
-  static constexpr int kStages = kFit > 4 ? 4 : kFit;
-  static_assert(kStages >= 2, "two stages must fit");
+  static constexpr int kTBytes = kXRows * 128 + 2048;
+  static constexpr int kFit = kRingBudget / (kWBytes + kTBytes);
+  static constexpr bool kSplit = kFit < 3 && 3 * kWBytes + 2 * kTBytes <= kRingBudget;
+  static constexpr int kWStages = kSplit ? 3 : (kFit > 4 ? 4 : kFit);
+  static constexpr int kTStages = kSplit ? 2 : kWStages;
+  static_assert(kTStages >= 2, "two stages must fit");
+  static_assert(kWStages * kWBytes + kTStages * kTBytes <= kRingBudget, "ring budget");
 };
 constexpr int kRingBytes = kRingBudget;
 
@@ -67,22 +73,28 @@ struct StageRef {
   uint32_t* scl;
 };
 
+// Weight part of ring slot sw and token part of ring slot st.
 template <int R, int NG>
-__device__ __forceinline__ StageRef stage_ref(uint8_t* ring, int s) {
+__device__ __forceinline__ StageRef stage_ref(uint8_t* ring, int sw, int st) {
   using G = Ring<R, NG>;
-  uint8_t* b = ring + s * G::kStageBytes;
-  return StageRef{b, b + G::kWBytes, reinterpret_cast<uint32_t*>(b + G::kWBytes + G::kXRows * 128)};
+  uint8_t* t = ring + G::kWStages * G::kWBytes + st * G::kTBytes;
+  return StageRef{ring + sw * G::kWBytes, t, reinterpret_cast<uint32_t*>(t + G::kXRows * 128)};
 }
 
 struct Lds {
+  // the K loop's operand ring; after the K loop the FP8 L1 epilogue keeps the amax of each
+  // (row group, token) in its last 4 KB (red)
   uint8_t ring[kRingBytes];
   int rowsrc[kTok];                           // source row of each tile row (token or pool row)
   int aux[kTok];                              // L1: top-k weight (f32 bits) / L2: slot row, per tile row
-  float red[4][kTok];                         // FP8 L1 epilogue: amax per (row group, token)
   float wsc[2][kMaxKBlocks];                  // FP8 recipe: weight-block scales per K block
   int2 td_next;                               // tile-list entry of the workgroup's next item
 };
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
+
+__device__ __forceinline__ float (*epilogue_red(Lds& L))[kTok] {
+  return reinterpret_cast<float(*)[kTok]>(L.ring + kRingBytes - 4 * kTok * sizeof(float));
+}
 
 // LDS-direct buffer loads: each active lane fetches `size` bytes at byte offset voff + soff of
 // the buffer into consecutive LDS bytes starting at the wave-uniform `lds` (lane i at
@@ -164,24 +176,25 @@ __device__ __forceinline__ int token_block(int w, int j) {
   return (NG & 1) && j == kTokenLoads<NG> - 1 && w >= 4 ? b - 4 : b;
 }
 
-// Load j of a wave's share of a stage: weights, then token blocks, then the scale word.
+// Load j of a wave's share of one K step's loads: the weight part of block bw into F.w and the
+// token part (token blocks, then the scale word) of block bt into F.x / F.scl.  With one ring
+// depth (bw == bt) the weights go first; with a deeper weight ring the token part goes first, so
+// that waiting for a block's token part leaves exactly the next block's weight loads in flight.
 template <int R, int NG>
-__device__ __forceinline__ void issue_load(const StageRef& S, const Src& s, int kb, int w, int j) {
+__device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int bw, int bt, int w, int j) {
   constexpr int NW = kWeightLoads<R>, NT = kTokenLoads<NG>;
-  if (j < NW) {
-    if (R == 0) lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 8 * j) * 128);
-    else lds_load16(s.wr, s.wo[j], kb * s.wkb, S.w + (32 * w + 16 * j) * 64);
-  } else if (j < NW + NT) {
-    lds_load16(s.xr, s.xo[j - NW], kb * 128, S.x + token_block<NG>(w, j - NW) * 8 * 128);
+  constexpr bool split = Ring<R, NG>::kSplit;
+  const bool is_w = split ? j > NT : j < NW;
+  const int jt = split ? j : j - NW;                 // index within the token part
+  const int jw = split ? j - NT - 1 : j;             // index within the weight part
+  if (is_w) {
+    if (R == 0) lds_load16(s.wr, s.wo[jw], bw * s.wkb, F.w + (32 * w + 8 * jw) * 128);
+    else lds_load16(s.wr, s.wo[jw], bw * s.wkb, F.w + (32 * w + 16 * jw) * 64);
+  } else if (jt < NT) {
+    lds_load16(s.xr, s.xo[jt], bt * 128, F.x + token_block<NG>(w, jt) * 8 * 128);
   } else {
-    lds_load4(s.cr, s.co, kb * s.ckb, S.scl + 64 * w);
+    lds_load4(s.cr, s.co, bt * s.ckb, F.scl + 64 * w);
   }
-}
-
-template <int R, int NG>
-__device__ __forceinline__ void issue_stage(const StageRef& S, const Src& s, int kb, int w) {
-#pragma unroll
-  for (int j = 0; j < kStageLoads<R, NG>; ++j) issue_load<R, NG>(S, s, kb, w, j);
 }
 
 // The stage loads of a K step go out behind the MFMAs of its column groups: after group i,
@@ -200,14 +213,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until this wave's loads of block kb have landed while the loads of the `newer` stages
-// issued after it (0 .. NS-2) may stay in flight.
-template <int R, int NG, int NS>
-__device__ __forceinline__ void wait_block(int newer) {
-  if (NS >= 4 && newer >= 2) wait_vmcnt<2 * kStageLoads<R, NG>>();
-  else if (NS >= 3 && newer >= 1) wait_vmcnt<kStageLoads<R, NG>>();
-  else wait_vmcnt<0>();
-}
+// Loads a wave may still have in flight once its loads of block kb have landed: step j issues
+// the token part of block j + NST - 1 and the weight part of block j + NSW - 1 (the prologue
+// plays the steps before 0), so with one depth NS the later NS - 2 steps' loads, and with
+// NSW = NST + 1 the weight part of block kb + 1 (issued after block kb's token part) and the
+// later NST - 2 steps' loads.
+template <int R, int NG>
+constexpr int kInFlight = Ring<R, NG>::kSplit
+                              ? kWeightLoads<R> + (Ring<R, NG>::kTStages - 2) * kStageLoads<R, NG>
+                              : (Ring<R, NG>::kWStages - 2) * kStageLoads<R, NG>;
 
 // LDS operand addressing.  Every row a lane reads has the same residue mod 16 (lr), so the
 // chunk swizzle is the same for all of them and a lane needs two base offsets per tile (the
@@ -240,7 +254,7 @@ __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
 template <int R, int NG, bool L1>
 __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const int wsel[4], int KB,
                                        v4f acc[4][NG], int w, int wn, int lane) {
-  constexpr int NS = Ring<R, NG>::kStages;
+  constexpr int NSW = Ring<R, NG>::kWStages, NST = Ring<R, NG>::kTStages;
   const int lr = lane & 15, lg = lane >> 4;
   const int tsp = tok_scale_pos(wn, lr);
   // lane offsets inside a stage's weight and token tiles
@@ -253,33 +267,41 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   int swrow[4];                            // MXFP4: scale word index of each weight tile's row
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
+  // Prologue: the issue of steps -(NSW - 1) .. -1.  Every step issues its loads without a
+  // branch; past the last block they fetch a copy of block KB - 1 into the slot of a retired
+  // block (never read), so the number of loads in flight behind block kb is always kInFlight.
+  static_assert(NSW == NST || NSW == NST + 1, "ring depths");
 #pragma unroll
-  for (int b = 0; b < NS - 1; ++b)
-    if (b < KB) issue_stage<R, NG>(stage_ref<R, NG>(L.ring, b), src, b, w);
-  // Every K step issues one stage: block kb + NS - 1, or past the end a copy of block KB - 1
-  // (into the slot of a retired block, never read), so that the issue has no branch and the
-  // number of stages in flight behind block kb is always min(NS - 1, KB) - 1.
-  const int newer = min(NS - 2, KB - 1);
-  int cur = 0;                           // ring slot of block kb
+  for (int j = -(NSW - 1); j < 0; ++j) {
+    const int bt = j + NST - 1, bw = j + NSW - 1;
+    const StageRef F = stage_ref<R, NG>(L.ring, bw, bt < 0 ? 0 : bt);
+#pragma unroll
+    for (int l = 0; l < kStageLoads<R, NG>; ++l) {
+      const bool is_w = Ring<R, NG>::kSplit ? l > kTokenLoads<NG> : l < kWeightLoads<R>;
+      if (is_w || bt >= 0) issue_load<R, NG>(F, src, min(bw, KB - 1), min(bt < 0 ? 0 : bt, KB - 1), w, l);
+    }
+  }
+  int cw = 0, ct = 0;                      // weight / token ring slots of block kb
   for (int kb = 0; kb < KB; ++kb) {
-    wait_block<R, NG, NS>(newer);
+    wait_vmcnt<kInFlight<R, NG>>();
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
-    // block kb + NS - 1 goes to the slot block kb-1 used.  Its loads are issued behind column
-    // group 0's MFMAs: issued right after the barrier, every wave's loads queue in the address
-    // unit at once and hold the waves back from their first MFMA.
-    const int ahead = min(kb + NS - 1, KB - 1);
-    int slot = cur + NS - 1;
-    slot = slot >= NS ? slot - NS : slot;
-    const StageRef F = stage_ref<R, NG>(L.ring, slot);
-    // fetch_part(i) issues the stage loads due after column group i: all of them after group
+    // the weight part of block kb + NSW - 1 and the token part of block kb + NST - 1 go to the
+    // slots block kb-1 used.  Their loads are issued behind column group 0's MFMAs: issued
+    // right after the barrier, every wave's loads queue in the address unit at once and hold
+    // the waves back from their first MFMA.
+    const int bw = min(kb + NSW - 1, KB - 1), bt = min(kb + NST - 1, KB - 1);
+    const int fw = cw == 0 ? NSW - 1 : cw - 1, ft = ct == 0 ? NST - 1 : ct - 1;
+    const StageRef F = stage_ref<R, NG>(L.ring, fw, ft);
+    // fetch_part(i) issues the loads due after column group i: all of them after group
     // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
     // the group loop's schedule.)
     auto fetch_part = [&](int i) {
 #pragma unroll
-      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG>(F, src, ahead, w, j);
+      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG>(F, src, bw, bt, w, j);
     };
-    const StageRef S = stage_ref<R, NG>(L.ring, cur);
-    cur = cur + 1 == NS ? 0 : cur + 1;
+    const StageRef S = stage_ref<R, NG>(L.ring, cw, ct);
+    cw = cw + 1 == NSW ? 0 : cw + 1;
+    ct = ct + 1 == NST ? 0 : ct + 1;
     const uint8_t* xl = S.x + xlo;
     const uint8_t* xh = S.x + xhi;
     // Column group 0's operands first and alone (10 LDS reads, so the waits before its MFMAs can
@@ -454,6 +476,10 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 8lg + 4t + r of the slab
   // for tile row 16(2i + wn) + lr.
   const bool do_clamp = a.clamp > 0.f;
+  // FP8: the group amax is reduced across the four row groups through the end of the ring, which
+  // other waves may still be reading (their last K block) or filling (copies past the end)
+  float(*red)[kTok] = epilogue_red(L);
+  if (R == 0) lds_barrier();
   float v[NG][2][4];
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
@@ -474,7 +500,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
     am = fmaxf(am, __shfl_xor(am, 16, 64));
     am = fmaxf(am, __shfl_xor(am, 32, 64));
     if (R == 0) {
-      if (lg == 0) L.red[wm][col] = am;
+      if (lg == 0) red[wm][col] = am;
     } else {
       // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
       const uint32_t code = ue8m0_for_amax(am);
@@ -498,7 +524,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int col = 16 * (2 * i + wn) + lr;
-      const float amax = fmaxf(fmaxf(L.red[0][col], L.red[1][col]), fmaxf(L.red[2][col], L.red[3][col]));
+      const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
       const float sf = amax / 448.0f, m = 448.0f / amax;
       const bool valid = col < cnt;
       uint2 q = make_uint2(0u, 0u);

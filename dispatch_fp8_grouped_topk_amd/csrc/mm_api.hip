@@ -207,6 +207,8 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   const int cus = device_cus();
   if (cus <= 0) return MEGA_MOE_ERR_HIP;
   a.large_grid = cus < 8 ? 8 : cus / 8 * 8;
+  a.quad = a.recipe == MEGA_MOE_RECIPE_MXFP4W_B32 && a.tile_mode == 0;
+  a.quad_grid = 2 * a.large_grid;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> bool {

@@ -43,7 +43,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Workspace header words.
-enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrWords = 64 };
+// kHdrTilesQuad: the first large-M tile (in list order) whose expert's first tile has at most
+// kQuadMaxNG column groups per wave; with the MXFP4 recipe, the L2 GEMM of the tiles from there
+// on runs in the four-wave kernel, two workgroups per CU.
+enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrTilesQuad = 3, kHdrWords = 64 };
+constexpr int kQuadMaxNG = 5;
 
 struct Args {
   // inputs
@@ -79,6 +83,8 @@ struct Args {
   int large_min_rows;   // auto mode: experts with at least this many rows use the large class
   int max_tiles_s, max_tiles_l;
   int large_grid;       // workgroups of the persistent large-M kernels (multiple of 8)
+  int quad;             // 1: MXFP4 L2 tiles of at most 160 rows go to the four-wave kernel
+  int quad_grid;        // its workgroups (two per CU, multiple of 8)
 };
 
 // ------------------------------------------------------------------------------------------

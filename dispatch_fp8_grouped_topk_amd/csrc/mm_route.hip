@@ -154,6 +154,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
       run += n;
     }
     s_class_base[0] = run;                     // total large tiles
+    a.hdr[kHdrTilesQuad] = s_class_base[kQuadMaxNG];   // tiles of the classes above kQuadMaxNG
   }
   __syncthreads();
   int carry = 0, carry_s = 0;

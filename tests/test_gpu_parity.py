@@ -71,6 +71,19 @@ def test_forced_tile_class(name, flags):
     _full_check(spec, synth.make_problem(spec), flags)
 
 
+def test_mxfp4_every_tile_size():
+    """MXFP4 experts of 1 to 10 row groups of 16 (the four-wave L2 kernel's tile sizes) beside a
+    601-row expert (three tiles of the eight-wave kernel), compared in full."""
+    counts = [1, 17, 33, 49, 65, 81, 97, 113, 129, 150, 160, 601]
+    T, k = sum(counts) // 2, 2
+    ids = np.repeat(np.arange(len(counts)), counts)           # sorted; no expert holds T pairs
+    idx = np.stack([ids[:T], ids[T:]], axis=1)                 # so each token's two differ
+    idx = idx[np.random.default_rng(117).permutation(T)].astype(np.int32)
+    assert (idx[:, 0] != idx[:, 1]).all()
+    spec = synth.Spec(T, 512, 256, len(counts), k, recipe=1, seed=117, weight_set=117)
+    _full_check(spec, _custom(spec, idx=idx))
+
+
 def test_all_tokens_on_one_expert():
     spec = synth.Spec(150, 512, 256, 8, 1, seed=110, weight_set=110)
     _full_check(spec, _custom(spec, idx=np.full((150, 1), 5)))

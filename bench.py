@@ -27,8 +27,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published (E2M1 x E4M3 runs at the FP8 rate)
 PHASES = ("dispatch", "l1_gemm_swiglu", "l2_gemm", "combine")
-# Kernel of each GEMM phase (default tile policy) and the sources that define it.
+# Kernels of each GEMM phase (default tile policy; MXFP4 L2 tiles of at most 160 rows run in the
+# four-wave kernel) and the sources that define them.
 PHASE_KERNEL = {"l1_gemm_swiglu": "k_large<L1>", "l2_gemm": "k_large<L2>"}
+PHASE_KERNEL_MXFP4 = {"l1_gemm_swiglu": "k_large<L1>", "l2_gemm": "k_large<L2> + k_quad_l2"}
 KERNEL_SOURCES = ("dispatch_fp8_grouped_topk_amd/csrc/mm_gemm_large.hip",
                   "dispatch_fp8_grouped_topk_amd/csrc/mm_common.h")
 TRAFFIC_FILE = os.path.join("profiles", "hbm_traffic.json")
@@ -242,7 +244,8 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = counted_traffic(dom, spec.name)
-    roof.update(kernel=PHASE_KERNEL[dom], phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
+    kernels = PHASE_KERNEL_MXFP4 if spec.recipe == 1 and args.flags == 0 else PHASE_KERNEL
+    roof.update(kernel=kernels[dom], phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
                 kernel_ms=round(phase_ms[dom], 4))
     out = {
         "metric": "MoE-layer TFLOP/s + weight GB/s vs roofline, H7168 I2048 256e top8",

@@ -282,6 +282,16 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     }
   }
   int cw = 0, ct = 0;                      // weight / token ring slots of block kb
+  // FP8: the last column group's promotion of block kb is done in step kb + 1, behind group 0's
+  // MFMAs, so that a wave reaches the barrier as soon as its last MFMAs are issued instead of
+  // after they have drained (same FMAs, same order: bit-identical sums)
+  v4f pend[4];
+  float pend_s[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    pend[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    pend_s[rt] = 0.f;
+  }
   for (int kb = 0; kb < KB; ++kb) {
     wait_vmcnt<kInFlight<R, NG>>();
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
@@ -338,6 +348,8 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
       read_token_scales();
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += pend[rt] * pend_s[rt];
       __builtin_amdgcn_sched_barrier(0);
       B = B1;
 #pragma unroll
@@ -364,7 +376,10 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       }
       const float sp = __uint_as_float(sw8[NG - 1]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += p[(NG - 1) & 1][rt] * (sp * cw[rt]);
+      for (int rt = 0; rt < 4; ++rt) {
+        pend[rt] = p[(NG - 1) & 1][rt];
+        pend_s[rt] = sp * cw[rt];
+      }
     } else {
       int swv[4];
 #pragma unroll
@@ -383,6 +398,10 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         if (i + 1 < NG) B = Bn;
       }
     }
+  }
+  if (R == 0) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += pend[rt] * pend_s[rt];
   }
   // the copies issued past the last block land in retired slots; let them land before the
   // item ends, so none can reach the LDS once the next item (or kernel) has laid it out anew

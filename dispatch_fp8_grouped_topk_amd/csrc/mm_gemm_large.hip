@@ -113,7 +113,7 @@ __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, int soff, voi
 
 // Workgroup barrier for the K pipeline.  Unlike __syncthreads() it carries no memory fence;
 // ordering is explicit instead: each wave waits for its own LDS-direct loads of the block about
-// to be read (wait_block) before arriving, such writes are complete in LDS once counted, and
+// to be read (wait_vmcnt) before arriving, such writes are complete in LDS once counted, and
 // the empty asm statements stop the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("" ::: "memory");
@@ -281,7 +281,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       if (is_w || bt >= 0) issue_load<R, NG>(F, src, min(bw, KB - 1), min(bt < 0 ? 0 : bt, KB - 1), w, l);
     }
   }
-  int cw = 0, ct = 0;                      // weight / token ring slots of block kb
+  int wslot = 0, tslot = 0;                // weight / token ring slots of block kb
   // FP8: the last column group's promotion of block kb is done in step kb + 1, behind group 0's
   // MFMAs, so that a wave reaches the barrier as soon as its last MFMAs are issued instead of
   // after they have drained (same FMAs, same order: bit-identical sums)
@@ -300,7 +300,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // right after the barrier, every wave's loads queue in the address unit at once and hold
     // the waves back from their first MFMA.
     const int bw = min(kb + NSW - 1, KB - 1), bt = min(kb + NST - 1, KB - 1);
-    const int fw = cw == 0 ? NSW - 1 : cw - 1, ft = ct == 0 ? NST - 1 : ct - 1;
+    const int fw = wslot == 0 ? NSW - 1 : wslot - 1, ft = tslot == 0 ? NST - 1 : tslot - 1;
     const StageRef F = stage_ref<R, NG>(L.ring, fw, ft);
     // fetch_part(i) issues the loads due after column group i: all of them after group
     // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
@@ -309,9 +309,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
       for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG>(F, src, bw, bt, w, j);
     };
-    const StageRef S = stage_ref<R, NG>(L.ring, cw, ct);
-    cw = cw + 1 == NSW ? 0 : cw + 1;
-    ct = ct + 1 == NST ? 0 : ct + 1;
+    const StageRef S = stage_ref<R, NG>(L.ring, wslot, tslot);
+    wslot = wslot + 1 == NSW ? 0 : wslot + 1;
+    tslot = tslot + 1 == NST ? 0 : tslot + 1;
     const uint8_t* xl = S.x + xlo;
     const uint8_t* xh = S.x + xhi;
     // Column group 0's operands first and alone (10 LDS reads, so the waits before its MFMAs can

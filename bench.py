@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one forward into a HIP graph and time --steps replays "
+                         "(reported as graph_ms_per_step; value stays the eager rate)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed region, run one elementwise float32 copy of this many MiB "
                          "(reads and writes exactly that many bytes) to calibrate HBM byte counters")
@@ -271,6 +274,24 @@ def main():
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "roofline": roof,
     }
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            mm.mega_moe_forward(*call)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            mm.mega_moe_forward(*call)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, P, min(args.cpu_tokens, spec.T))
     print(json.dumps(out), flush=True)

@@ -28,6 +28,7 @@ RECIPE_MXFP4W_B32 = 1
 FLAG_TILE_AUTO = 0
 FLAG_TILE_SMALL = 1
 FLAG_TILE_LARGE = 2
+FLAG_CLAMP_INPUTS = 4   # with swiglu_clamp > 0: clamp gate and up before SiLU
 
 ABI_VERSION = 1
 

@@ -32,7 +32,7 @@ int check_problem(const mega_moe_problem* p) {
   if (p->topk < 1 || p->topk > mm::kMaxTopk) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->recipe != MEGA_MOE_RECIPE_FP8_B128 && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32) return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
-  if (p->flags & ~MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS)) return MEGA_MOE_ERR_INVALID_ARG;
   if ((p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->num_tokens * (int64_t)p->topk > (int64_t)(INT_MAX / 2)) return MEGA_MOE_ERR_INVALID_ARG;
   return MEGA_MOE_OK;
@@ -197,6 +197,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.NB = L.NB;
   a.recipe = p->recipe;
   a.clamp = std::isinf(p->swiglu_clamp) ? 0.f : p->swiglu_clamp;
+  a.clamp_inputs = (p->flags & MEGA_MOE_FLAG_CLAMP_INPUTS) != 0;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
   a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;

@@ -79,6 +79,7 @@ struct Args {
   int T, H, I, E, k, P, NB;
   int recipe;
   float clamp;          // <= 0: none
+  int clamp_inputs;     // 1: clamp gate and up before SiLU instead of silu(g)*u
   int tile_mode;        // 0 auto, 1 small only, 2 large only
   int large_min_rows;   // auto mode: experts with at least this many rows use the large class
   int max_tiles_s, max_tiles_l;
@@ -108,6 +109,17 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // silu(g) = g / (1 + exp(-g)) with the hardware exp and reciprocal instructions (float32 to a
 // few ulp); where exp(-g) overflows (g below about -88) the result is -0, as in the exact form.
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// silu(g) * u with the problem's clamp c > 0: on g and u before SiLU (inputs) or on the product.
+__device__ __forceinline__ float swiglu_f32(float g, float u, float c, bool clamp_in, bool clamp_out) {
+  if (clamp_in) {
+    g = fminf(fmaxf(g, -c), c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  float s = silu_f32(g) * u;
+  if (clamp_out) s = fminf(fmaxf(s, -c), c);
+  return s;
+}
 
 // E4M3 codes of four values divided by sf = amax / 448 (amax > 0): multiplied by m = 448 / amax,
 // one IEEE division per group instead of one per value (the product is within about one ulp of

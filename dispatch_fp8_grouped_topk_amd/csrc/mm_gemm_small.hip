@@ -160,7 +160,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
   // ---------------- epilogue: SwiGLU, clamp, top-k weight, group amax, scale, E4M3 cast
   // acc[i][s][r] (gate) and acc[2+i][s][r] (up) are channel 32w + 16i + 4lg + r of the slab
   // for pool row 16s + lr of the tile.
-  const bool do_clamp = a.clamp > 0.f;
+  const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
   float v[NSUB][2][4];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -172,8 +172,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[i][s][r], u = acc[2 + i][s][r];
-        float sv = silu_f32(g) * u;
-        if (do_clamp) sv = fminf(fmaxf(sv, -a.clamp), a.clamp);
+        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out);
         const float x = sv * wt;
         v[s][i][r] = x;
         am = fmaxf(am, fabsf(x));

@@ -72,11 +72,17 @@ typedef enum {
 
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
-   2 = large-M class only); other bits must be 0. */
+   2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS; other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
 #define MEGA_MOE_FLAG_TILE_MASK  3u
+/* flags bit 2: with swiglu_clamp = c > 0, clamp the gate and up halves of the L1 result to
+ * [-c, c] before SiLU and leave silu(g)*u unclamped (the activation clamp of the design page
+ * "MegaMoE SM90 Implementation Design", section 10.1, step 3).  Without it, c clamps
+ * silu(g)*u, the reading of the mid-size workload's "SwiGLU output clamped".  Ignored when
+ * there is no clamp. */
+#define MEGA_MOE_FLAG_CLAMP_INPUTS 4u
 
 enum {
   MEGA_MOE_OK = 0,
@@ -96,7 +102,8 @@ typedef struct {
   int32_t topk;          /* k in [1, 64] columns of topk_idx / topk_w */
   int32_t recipe;        /* mega_moe_recipe */
   float swiglu_clamp;    /* 0 or +inf: no clamp; c > 0: silu(g)*u clamped to [-c, c]
-                            before the top-k weight multiplies it */
+                            before the top-k weight multiplies it (or, with
+                            MEGA_MOE_FLAG_CLAMP_INPUTS, gate and up clamped before SiLU) */
   uint32_t flags;        /* MEGA_MOE_FLAG_* */
 } mega_moe_problem;
 

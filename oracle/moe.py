@@ -22,7 +22,9 @@ What it computes, step by step, with where the pages define each step:
    32-wide K blocks with power-of-two scales on both operands (PR #411).
 3. SwiGLU epilogue (design page section 10.1 "Register-Based Flow"):
    s = silu(gate) * up with gate = acc[:, :I], up = acc[:, I:]; optionally
-   clamped; multiplied by the row's top-k weight before the re-quantisation.
+   clamped (s to [-c, c], or, as in step 3 of that section, gate and up to
+   [-c, c] before SiLU); multiplied by the row's top-k weight before the
+   re-quantisation.
 4. Re-quantisation per group of G output channels: amax, float scale
    amax/448 and an E4M3 cast of value/scale (design section 10.1 steps 4-5,
    G = 128), or a power-of-two UE8M0 scale per 32 channels for the MXFP4 recipe.
@@ -59,6 +61,7 @@ class Problem:
     k: int
     recipe: int = RECIPE_FP8_B128
     swiglu_clamp: float = 0.0
+    clamp_inputs: bool = False     # clamp gate and up before SiLU instead of silu(gate) * up
 
     @property
     def group(self) -> int:
@@ -136,14 +139,20 @@ def block_scaled_gemm(prob: Problem, a_vals, a_scale, b_vals, b_scale) -> np.nda
 
 # --------------------------------------------------------------------------- epilogue
 def swiglu_weighted(prob: Problem, acc: np.ndarray, w_rows: np.ndarray) -> np.ndarray:
-    """s = silu(gate) * up, clamped to [-c, c] when c > 0, times the top-k weight (float64)."""
+    """s = silu(gate) * up times the top-k weight (float64).  With a clamp c > 0, s is clamped
+    to [-c, c]; with clamp_inputs, gate and up are clamped to [-c, c] before SiLU instead (the
+    design page's activation clamp, section 10.1 step 3)."""
     I = prob.I
     gate = acc[:, :I]
     up = acc[:, I:2 * I]
+    c = prob.swiglu_clamp
+    clamp = c > 0 and np.isfinite(c)
+    if clamp and prob.clamp_inputs:
+        gate = np.clip(gate, -c, c)
+        up = np.clip(up, -c, c)
     with np.errstate(over="ignore"):
         s = gate / (1.0 + np.exp(-gate)) * up          # exp overflow -> silu(gate) = -0
-    c = prob.swiglu_clamp
-    if c > 0 and np.isfinite(c):
+    if clamp and not prob.clamp_inputs:
         s = np.clip(s, -c, c)
     return s * np.asarray(w_rows, dtype=np.float32).astype(np.float64)[:, None]
 

@@ -47,6 +47,7 @@ class Spec:
     recipe: int = RECIPE_FP8
     routing: str = "uniform"   # uniform | biased | zipf | uniform_shared
     swiglu_clamp: float = 0.0
+    clamp_inputs: bool = False     # the clamp applies to gate and up before SiLU
     seed: int = 1000
     weight_set: int = 0
     w_std: float = 0.02

@@ -26,11 +26,13 @@ CODE_MISMATCH_FRAC = 5e-3
 
 
 def problem_of(spec: synth.Spec, flags: int = 0) -> mm.Problem:
+    flags |= mm.FLAG_CLAMP_INPUTS if spec.clamp_inputs else 0
     return mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, flags)
 
 
 def oracle_problem(spec: synth.Spec) -> oracle.Problem:
-    return oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp)
+    return oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp,
+                          spec.clamp_inputs)
 
 
 def to_device(P: dict, device="cuda") -> dict:

@@ -52,6 +52,11 @@ SMALL = {
     "mxfp4": synth.Spec(40, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=107, weight_set=107),
     "mxfp4_multi_tile": synth.Spec(200, 512, 256, 3, 2, recipe=1, seed=108, weight_set=108),
     "mxfp4_clamp": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.05, seed=109, weight_set=109),
+    # the activation clamp on gate and up (flag MEGA_MOE_FLAG_CLAMP_INPUTS)
+    "clamp_inputs": synth.Spec(64, 512, 256, 8, 4, routing="biased", swiglu_clamp=0.3, clamp_inputs=True,
+                               seed=122, weight_set=122),
+    "mxfp4_clamp_inputs": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.3, clamp_inputs=True,
+                                     seed=123, weight_set=123),
     # more than 16384 pairs: dispatch runs 1024 pairs per workgroup; skewed so that experts
     # fill every large-M column-group class
     "wide_dispatch": synth.Spec(2100, 512, 256, 64, 8, routing="zipf", seed=115, weight_set=115),
@@ -65,7 +70,8 @@ def test_small_problem_full_parity(name):
 
 
 @pytest.mark.parametrize("flags", [1, 2], ids=["small_only", "large_only"])
-@pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile"])
+@pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile", "clamp_inputs",
+                                  "mxfp4_clamp_inputs"])
 def test_forced_tile_class(name, flags):
     spec = SMALL[name]
     _full_check(spec, synth.make_problem(spec), flags)

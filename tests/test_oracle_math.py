@@ -28,7 +28,8 @@ def _np(P):
 
 
 def _prob(spec):
-    return oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp)
+    return oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp,
+                          spec.clamp_inputs)
 
 
 # ----------------------------------------------------------------------------- brute force
@@ -108,9 +109,11 @@ def brute_force(spec, P):
             v32 = []
             for i in range(I):
                 g, u = acc[i], acc[I + i]
-                sv = g / (1.0 + math.exp(-g)) * u
                 c = spec.swiglu_clamp
-                if c > 0:
+                if c > 0 and spec.clamp_inputs:          # activation clamp on gate and up
+                    g, u = min(max(g, -c), c), min(max(u, -c), c)
+                sv = g / (1.0 + math.exp(-g)) * u
+                if c > 0 and not spec.clamp_inputs:      # clamp on silu(g) * u
                     sv = min(max(sv, -c), c)
                 v32.append(np.float32(sv * float(np.float32(tw[t, j]))))
             # re-quantisation, group by group
@@ -151,6 +154,9 @@ BRUTE_SPECS = {
     "fp8_clamp": synth.Spec(3, 256, 128, 3, 2, seed=12, weight_set=12, swiglu_clamp=0.01),
     "mxfp4": synth.Spec(3, 256, 128, 3, 2, recipe=1, seed=13, weight_set=13),
     "mxfp4_shared": synth.Spec(2, 128, 64, 3, 2, recipe=1, routing="uniform_shared", seed=14, weight_set=14),
+    "fp8_clamp_inputs": synth.Spec(3, 256, 128, 3, 2, seed=15, weight_set=15, swiglu_clamp=0.2, clamp_inputs=True),
+    "mxfp4_clamp_inputs": synth.Spec(3, 256, 128, 3, 2, recipe=1, seed=16, weight_set=16, swiglu_clamp=0.2,
+                                     clamp_inputs=True),
 }
 
 
@@ -215,6 +221,31 @@ def test_clamp_applies_before_topk_weight():
     acc = np.array([[50.0, -50.0, 50.0, 50.0]])       # s = [~2500, ~-0]
     got = oracle.swiglu_weighted(prob, acc, np.array([0.5], np.float32))
     assert got[0, 0] == 5.0                             # clamp(2500) = 10, then * 0.5
+
+
+def test_input_clamp_applies_to_gate_and_up():
+    # design page section 10.1 step 3: gate and up clamped to [-c, c] before SiLU.  gate (50, -50)
+    # and up (50, 50) with c = 10 become (10, -10) and (10, 10):
+    #   silu(10) * 10 * 0.5  = 10 / (1 + e^-10) * 5 = 50 / 1.0000453999297625 = 49.99773010656487
+    #   silu(-10) * 10 * 0.5 = -10 / (1 + e^10) * 5 = -50 / 22027.465794806718 = -0.0022698934351217193
+    prob = oracle.Problem(1, 128, 2, 1, 1, swiglu_clamp=10.0, clamp_inputs=True)
+    acc = np.array([[50.0, -50.0, 50.0, 50.0]])
+    got = oracle.swiglu_weighted(prob, acc, np.array([0.5], np.float32))
+    np.testing.assert_allclose(got[0], [49.99773010656487, -0.0022698934351217193], rtol=1e-13)
+    # the product is not clamped (49.998 > 10), unlike the output clamp (first row: 5.0)
+    assert got[0, 0] > 10.0
+
+
+@pytest.mark.parametrize("recipe", [0, 1])
+def test_input_clamp_above_every_accumulator_changes_nothing(recipe):
+    spec = synth.Spec(6, 512, 256, 5, 2, recipe=recipe, seed=17, weight_set=17)
+    P = _np(synth.make_problem(spec))
+    base = oracle.forward(_prob(spec), **P)
+    wide = oracle.forward(oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, 1e30, True), **P)
+    assert np.array_equal(base["y"], wide["y"])
+    # a clamp that binds changes the output
+    tight = oracle.forward(oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, 0.05, True), **P)
+    assert not np.array_equal(base["y"], tight["y"])
 
 
 # ----------------------------------------------------------------------------- re-quantisation

@@ -29,6 +29,7 @@ FLAG_TILE_AUTO = 0
 FLAG_TILE_SMALL = 1
 FLAG_TILE_LARGE = 2
 FLAG_CLAMP_INPUTS = 4   # with swiglu_clamp > 0: clamp gate and up before SiLU
+FLAG_PRECISE_SILU = 8   # SiLU with expf and IEEE division instead of the hardware exp / rcp
 
 ABI_VERSION = 1
 
@@ -89,6 +90,8 @@ def _load():
     lib.mega_moe_workspace_views.argtypes = [P, vp, ctypes.POINTER(_Views)]
     lib.mega_moe_forward.restype = ctypes.c_int
     lib.mega_moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.mega_moe_forward_stats.restype = ctypes.c_int
+    lib.mega_moe_forward_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.mega_moe_forward_profiled.restype = ctypes.c_int
     lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -154,9 +157,12 @@ NUM_PHASE_EVENTS = 5
 
 
 def mega_moe_forward(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
-                     workspace, stream=None) -> None:
-    """Enqueue the layer forward on ``stream`` (default: torch's current stream of x's device)."""
-    _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, None)
+                     workspace, stream=None, recv_stats=None) -> None:
+    """Enqueue the layer forward on ``stream`` (default: torch's current stream of x's device).
+    recv_stats: optional int32 [E] device tensor to which each expert's received row count is
+    added (mega_moe_forward_stats)."""
+    _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, None,
+             recv_stats)
 
 
 def mega_moe_forward_profiled(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
@@ -166,7 +172,8 @@ def mega_moe_forward_profiled(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w,
     _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, events)
 
 
-def _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, events):
+def _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, events,
+             recv_stats=None):
     import torch
     dev = x.device
     if dev.type != "cuda":
@@ -186,7 +193,11 @@ def _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, wo
     args = (ctypes.byref(problem), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_w),
             _ptr(l1_w), _ptr(l1_sf), _ptr(l2_w), _ptr(l2_sf), _ptr(y),
             _ptr(workspace), nbytes, ctypes.c_void_p(handle))
-    if events is None:
+    if recv_stats is not None:
+        _check_tensor("recv_stats", recv_stats, dev, (torch.int32,), (problem.num_experts,))
+        st = _load().mega_moe_forward_stats(*args[:-1], _ptr(recv_stats), args[-1])
+        what = "mega_moe_forward_stats"
+    elif events is None:
         st = _load().mega_moe_forward(*args)
         what = "mega_moe_forward"
     else:

@@ -32,7 +32,8 @@ int check_problem(const mega_moe_problem* p) {
   if (p->topk < 1 || p->topk > mm::kMaxTopk) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->recipe != MEGA_MOE_RECIPE_FP8_B128 && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32) return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
-  if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS)) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU))
+    return MEGA_MOE_ERR_INVALID_ARG;
   if ((p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->num_tokens * (int64_t)p->topk > (int64_t)(INT_MAX / 2)) return MEGA_MOE_ERR_INVALID_ARG;
   return MEGA_MOE_OK;
@@ -149,7 +150,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
                  const int32_t* topk_idx, const float* topk_w, const void* l1_w,
                  const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events,
-                 int num_events) {
+                 int num_events, int32_t* recv_stats) {
   int st = check_problem(p);
   if (st) return st;
   const Layout L = make_layout(p);
@@ -173,6 +174,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.l2_w = static_cast<const uint8_t*>(l2_w);
   a.l2_sf = l2_sf;
   a.y = static_cast<uint16_t*>(y);
+  a.recv_stats = recv_stats;
   uint8_t* w = static_cast<uint8_t*>(workspace);
   a.hdr = reinterpret_cast<int32_t*>(w + L.hdr);
   a.count = reinterpret_cast<int32_t*>(w + L.count);
@@ -198,6 +200,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.recipe = p->recipe;
   a.clamp = std::isinf(p->swiglu_clamp) ? 0.f : p->swiglu_clamp;
   a.clamp_inputs = (p->flags & MEGA_MOE_FLAG_CLAMP_INPUTS) != 0;
+  a.precise_silu = (p->flags & MEGA_MOE_FLAG_PRECISE_SILU) != 0;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
   a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;
@@ -231,7 +234,17 @@ MM_EXPORT int mega_moe_forward(const mega_moe_problem* p, const void* x, const v
                                const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
                                void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
-                      workspace_bytes, stream, nullptr, 0);
+                      workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+MM_EXPORT int mega_moe_forward_stats(const mega_moe_problem* p, const void* x, const void* x_sf,
+                                     const int32_t* topk_idx, const float* topk_w, const void* l1_w,
+                                     const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t* cumulative_expert_recv_stats, void* stream) {
+  if ((reinterpret_cast<uintptr_t>(cumulative_expert_recv_stats) & 3u) != 0) return MEGA_MOE_ERR_MISALIGNED;
+  return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
+                      workspace_bytes, stream, nullptr, 0, cumulative_expert_recv_stats);
 }
 
 MM_EXPORT int mega_moe_forward_profiled(const mega_moe_problem* p, const void* x, const void* x_sf,
@@ -245,5 +258,5 @@ MM_EXPORT int mega_moe_forward_profiled(const mega_moe_problem* p, const void* x
   for (int i = 0; i < num_events; ++i)
     if (!events[i]) return MEGA_MOE_ERR_NULL_POINTER;
   return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
-                      workspace_bytes, stream, events, num_events);
+                      workspace_bytes, stream, events, num_events, nullptr);
 }

@@ -60,6 +60,7 @@ struct Args {
   const uint8_t* l2_w;
   const void* l2_sf;
   uint16_t* y;
+  int32_t* recv_stats;  // [E] cumulative per-expert received rows (NULL: none)
   // workspace regions
   int32_t* hdr;
   int32_t* count;       // [E]
@@ -80,6 +81,7 @@ struct Args {
   int recipe;
   float clamp;          // <= 0: none
   int clamp_inputs;     // 1: clamp gate and up before SiLU instead of silu(g)*u
+  int precise_silu;     // 1: SiLU with expf and an IEEE division (else hardware exp / rcp)
   int tile_mode;        // 0 auto, 1 small only, 2 large only
   int large_min_rows;   // auto mode: experts with at least this many rows use the large class
   int max_tiles_s, max_tiles_l;
@@ -110,13 +112,15 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // few ulp); where exp(-g) overflows (g below about -88) the result is -0, as in the exact form.
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// silu(g) * u with the problem's clamp c > 0: on g and u before SiLU (inputs) or on the product.
-__device__ __forceinline__ float swiglu_f32(float g, float u, float c, bool clamp_in, bool clamp_out) {
+// silu(g) * u with the problem's clamp c > 0: on g and u before SiLU (inputs) or on the product;
+// precise: SiLU with the device library's expf and an IEEE division.
+__device__ __forceinline__ float swiglu_f32(float g, float u, float c, bool clamp_in, bool clamp_out,
+                                            bool precise) {
   if (clamp_in) {
     g = fminf(fmaxf(g, -c), c);
     u = fminf(fmaxf(u, -c), c);
   }
-  float s = silu_f32(g) * u;
+  float s = (precise ? g / (1.0f + expf(-g)) : silu_f32(g)) * u;
   if (clamp_out) s = fminf(fmaxf(s, -c), c);
   return s;
 }

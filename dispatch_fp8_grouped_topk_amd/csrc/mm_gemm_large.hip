@@ -495,6 +495,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 8lg + 4t + r of the slab
   // for tile row 16(2i + wn) + lr.
   const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
+  const bool precise = a.precise_silu;
   // FP8: the group amax is reduced across the four row groups through the end of the ring, which
   // other waves may still be reading (their last K block) or filling (copies past the end)
   float(*red)[kTok] = epilogue_red(L);
@@ -510,7 +511,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[t][i][r], u = acc[2 + t][i][r];
-        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out);
+        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out, precise);
         const float x = sv * wt;
         v[i][t][r] = x;
         am = fmaxf(am, fabsf(x));

@@ -161,6 +161,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
   // acc[i][s][r] (gate) and acc[2+i][s][r] (up) are channel 32w + 16i + 4lg + r of the slab
   // for pool row 16s + lr of the tile.
   const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
+  const bool precise = a.precise_silu;
   float v[NSUB][2][4];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -172,7 +173,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[i][s][r], u = acc[2 + i][s][r];
-        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out);
+        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out, precise);
         const float x = sv * wt;
         v[s][i][r] = x;
         am = fmaxf(am, fabsf(x));

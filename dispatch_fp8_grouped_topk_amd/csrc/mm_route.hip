@@ -180,6 +180,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     __syncthreads();
     if (e < E) {
       a.count[e] = c;
+      if (a.recv_stats) a.recv_stats[e] += c;
       a.offset[e] = carry + inc - c;
       const int bs = carry_s + inc_s - nts;
       for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);

@@ -72,7 +72,8 @@ typedef enum {
 
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
-   2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS; other bits must be 0. */
+   2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU;
+   other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
@@ -83,6 +84,10 @@ typedef enum {
  * silu(g)*u, the reading of the mid-size workload's "SwiGLU output clamped".  Ignored when
  * there is no clamp. */
 #define MEGA_MOE_FLAG_CLAMP_INPUTS 4u
+/* flags bit 3: SiLU with the device library's expf and an IEEE division (the pages' fast_math =
+ * false, design page section 10.1 step 3); by default the hardware exp and reciprocal
+ * instructions (fast_math = true), float32 to a few ulp. */
+#define MEGA_MOE_FLAG_PRECISE_SILU 8u
 
 enum {
   MEGA_MOE_OK = 0,
@@ -147,6 +152,21 @@ int mega_moe_forward_profiled(const mega_moe_problem* p,
                               const void* l2_w, const void* l2_sf,
                               void* y, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* events, int num_events);
+
+/* mega_moe_forward that also adds each expert's received row count (its pool size: pairs
+   routed to it, masked and invalid slots excluded) of this call to the caller's device array
+   cumulative_expert_recv_stats[E] (int32), the per-expert receive statistics of the research
+   report's and the design page's interface (`cumulative_local_expert_recv_stats`; design page
+   section 10.2).  The array is never cleared by the library; NULL skips the update.  The add
+   runs on `stream` after the dispatch counts are known; calls that share one array must be
+   ordered on one stream (concurrent calls race on it). */
+int mega_moe_forward_stats(const mega_moe_problem* p,
+                           const void* x, const void* x_sf,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const void* l1_w, const void* l1_sf,
+                           const void* l2_w, const void* l2_sf,
+                           void* y, void* workspace, size_t workspace_bytes,
+                           int32_t* cumulative_expert_recv_stats, void* stream);
 
 /* Fill *out with device pointers into `workspace` for problem p. */
 int mega_moe_workspace_views(const mega_moe_problem* p, const void* workspace,

@@ -59,15 +59,15 @@ def test_workspace_size_grows_with_tokens_and_covers_buffers():
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
                                 dict(k=65), dict(recipe=2), dict(clamp=-1.0), dict(clamp=float("nan")),
-                                dict(flags=8), dict(flags=3), dict(flags=7), dict(T=-1), dict(H=32768)])
+                                dict(flags=16), dict(flags=3), dict(flags=15), dict(T=-1), dict(H=32768)])
 def test_invalid_problem_rejected(kw):
     with pytest.raises(mm.MegaMoEError) as ei:
         mm.mega_moe_workspace_size(_p(**kw))
     assert ei.value.status == -1
 
 
-def test_clamp_inputs_flag_accepted_with_either_tile_class():
-    for flags in (4, 5, 6):
+def test_numerics_flags_accepted_with_either_tile_class():
+    for flags in (4, 5, 6, 8, 12, 14):
         assert mm.mega_moe_workspace_size(_p(clamp=1.0, flags=flags)) > 0
 
 

@@ -69,6 +69,15 @@ def test_small_problem_full_parity(name):
     _full_check(spec, synth.make_problem(spec))
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2], ids=["auto", "small_only", "large_only"])
+@pytest.mark.parametrize("name", ["ragged", "clamp", "mxfp4_clamp", "zipf"])
+def test_precise_silu(name, flags):
+    """MEGA_MOE_FLAG_PRECISE_SILU (expf and IEEE division): the same bar against the oracle."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    spec = SMALL[name]
+    _full_check(spec, synth.make_problem(spec), flags | mm.FLAG_PRECISE_SILU)
+
+
 @pytest.mark.parametrize("flags", [1, 2], ids=["small_only", "large_only"])
 @pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile", "clamp_inputs",
                                   "mxfp4_clamp_inputs"])
@@ -103,6 +112,35 @@ def test_masked_and_invalid_ids():
     idx[rng.random(idx.shape) < 0.2] = -1
     idx[rng.random(idx.shape) < 0.1] = 6 + 3
     _full_check(spec, _custom(spec, idx=idx))
+
+
+@pytest.mark.parametrize("recipe", [0, 1])
+def test_cumulative_expert_recv_stats(recipe):
+    """mega_moe_forward_stats adds each expert's received rows (masked and invalid slots
+    excluded) to the caller's array, call after call, and leaves y unchanged."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    import oracle
+    from harness import problem_of
+    spec = synth.Spec(40, 512, 256, 7, 3, recipe=recipe, seed=124 + recipe, weight_set=124 + recipe)
+    P = synth.make_problem(spec)
+    idx = P["topk_idx"].numpy().copy()
+    rng = np.random.default_rng(1)
+    idx[rng.random(idx.shape) < 0.2] = -1
+    idx[rng.random(idx.shape) < 0.1] = 7 + 2
+    D = to_device(_custom(spec, idx=idx))
+    prob = problem_of(spec)
+    ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device="cuda")
+    args = (prob, D["x"], D["x_sf"], D["topk_idx"], D["topk_w"], D["l1_w"], D["l1_sf"], D["l2_w"], D["l2_sf"])
+    y0 = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device="cuda")
+    mm.mega_moe_forward(*args, y0, ws)
+    stats = torch.full((spec.E,), 5, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(y0)
+    for _ in range(2):
+        mm.mega_moe_forward(*args, y, ws, recv_stats=stats)
+    torch.cuda.synchronize()
+    count = oracle.route(idx, spec.E)["count"]
+    assert np.array_equal(stats.cpu().numpy(), 5 + 2 * np.asarray(count, dtype=np.int64))
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
 
 
 def test_empty_experts_and_skew():

@@ -112,15 +112,22 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // few ulp); where exp(-g) overflows (g below about -88) the result is -0, as in the exact form.
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // silu(g) * u with the problem's clamp c > 0: on g and u before SiLU (inputs) or on the product;
-// precise: SiLU with the device library's expf and an IEEE division.
-__device__ __forceinline__ float swiglu_f32(float g, float u, float c, bool clamp_in, bool clamp_out,
-                                            bool precise) {
+// kPrecise: SiLU with the device library's expf and an IEEE division.  The caller picks the
+// instantiation with one wave-uniform branch around its whole epilogue, so the default path
+// carries no trace of the precise one.
+template <bool kPrecise>
+__device__ __forceinline__ float swiglu_f32(float g, float u, float c, bool clamp_in, bool clamp_out) {
   if (clamp_in) {
     g = fminf(fmaxf(g, -c), c);
     u = fminf(fmaxf(u, -c), c);
   }
-  float s = (precise ? g / (1.0f + expf(-g)) : silu_f32(g)) * u;
+  float s = (kPrecise ? g / (1.0f + expf(-g)) : silu_f32(g)) * u;
   if (clamp_out) s = fminf(fmaxf(s, -c), c);
   return s;
 }

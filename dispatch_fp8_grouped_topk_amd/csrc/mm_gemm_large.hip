@@ -495,49 +495,53 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 8lg + 4t + r of the slab
   // for tile row 16(2i + wn) + lr.
   const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
-  const bool precise = a.precise_silu;
   // FP8: the group amax is reduced across the four row groups through the end of the ring, which
   // other waves may still be reading (their last K block) or filling (copies past the end)
   float(*red)[kTok] = epilogue_red(L);
   if (R == 0) lds_barrier();
   float v[NG][2][4];
+  // one instantiation of the SwiGLU pass per SiLU form, chosen by one wave-uniform branch
+  auto swiglu_pass = [&](auto precise) {
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int col = 16 * (2 * i + wn) + lr;
-    const float wt = col < cnt ? __int_as_float(L.aux[col]) : 0.f;
-    float am = 0.f;
+    for (int i = 0; i < NG; ++i) {
+      const int col = 16 * (2 * i + wn) + lr;
+      const float wt = col < cnt ? __int_as_float(L.aux[col]) : 0.f;
+      float am = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = acc[t][i][r], u = acc[2 + t][i][r];
-        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out, precise);
-        const float x = sv * wt;
-        v[i][t][r] = x;
-        am = fmaxf(am, fabsf(x));
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[t][i][r], u = acc[2 + t][i][r];
+          const float sv = swiglu_f32<decltype(precise)::value>(g, u, a.clamp, clamp_in, clamp_out);
+          const float x = sv * wt;
+          v[i][t][r] = x;
+          am = fmaxf(am, fabsf(x));
+        }
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      if (R == 0) {
+        if (lg == 0) red[wm][col] = am;
+      } else {
+        // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
+        const uint32_t code = ue8m0_for_amax(am);
+        const int ex = 127 - (int)code;
+        const bool valid = col < cnt;
+        uint2 q = make_uint2(0u, 0u);
+        if (am > 0.f) {
+          q.x = pack_fp8x4(clamp448(ldexpf(v[i][0][0], ex)), clamp448(ldexpf(v[i][0][1], ex)),
+                           clamp448(ldexpf(v[i][0][2], ex)), clamp448(ldexpf(v[i][0][3], ex)));
+          q.y = pack_fp8x4(clamp448(ldexpf(v[i][1][0], ex)), clamp448(ldexpf(v[i][1][1], ex)),
+                           clamp448(ldexpf(v[i][1][2], ex)), clamp448(ldexpf(v[i][1][3], ex)));
+        }
+        if (valid)
+          *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
+        if (valid && lg == 0)
+          static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + wm] = (uint8_t)code;
       }
-    am = fmaxf(am, __shfl_xor(am, 16, 64));
-    am = fmaxf(am, __shfl_xor(am, 32, 64));
-    if (R == 0) {
-      if (lg == 0) red[wm][col] = am;
-    } else {
-      // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
-      const uint32_t code = ue8m0_for_amax(am);
-      const int ex = 127 - (int)code;
-      const bool valid = col < cnt;
-      uint2 q = make_uint2(0u, 0u);
-      if (am > 0.f) {
-        q.x = pack_fp8x4(clamp448(ldexpf(v[i][0][0], ex)), clamp448(ldexpf(v[i][0][1], ex)),
-                         clamp448(ldexpf(v[i][0][2], ex)), clamp448(ldexpf(v[i][0][3], ex)));
-        q.y = pack_fp8x4(clamp448(ldexpf(v[i][1][0], ex)), clamp448(ldexpf(v[i][1][1], ex)),
-                         clamp448(ldexpf(v[i][1][2], ex)), clamp448(ldexpf(v[i][1][3], ex)));
-      }
-      if (valid)
-        *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
-      if (valid && lg == 0)
-        static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + wm] = (uint8_t)code;
     }
-  }
+  };
+  if (a.precise_silu) swiglu_pass(BoolC<true>{});
+  else swiglu_pass(BoolC<false>{});
   if (R == 0) {
     __syncthreads();
 #pragma unroll

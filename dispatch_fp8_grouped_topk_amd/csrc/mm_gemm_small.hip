@@ -161,45 +161,49 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
   // acc[i][s][r] (gate) and acc[2+i][s][r] (up) are channel 32w + 16i + 4lg + r of the slab
   // for pool row 16s + lr of the tile.
   const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
-  const bool precise = a.precise_silu;
   float v[NSUB][2][4];
+  // one instantiation of the SwiGLU pass per SiLU form, chosen by one wave-uniform branch
+  auto swiglu_pass = [&](auto precise) {
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int col = 16 * s + lr;
-    const float wt = col < cnt ? a.w_pool[off + col] : 0.f;
-    float am = 0.f;
+    for (int s = 0; s < NSUB; ++s) {
+      const int col = 16 * s + lr;
+      const float wt = col < cnt ? a.w_pool[off + col] : 0.f;
+      float am = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = acc[i][s][r], u = acc[2 + i][s][r];
-        const float sv = swiglu_f32(g, u, a.clamp, clamp_in, clamp_out, precise);
-        const float x = sv * wt;
-        v[s][i][r] = x;
-        am = fmaxf(am, fabsf(x));
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[i][s][r], u = acc[2 + i][s][r];
+          const float sv = swiglu_f32<decltype(precise)::value>(g, u, a.clamp, clamp_in, clamp_out);
+          const float x = sv * wt;
+          v[s][i][r] = x;
+          am = fmaxf(am, fabsf(x));
+        }
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      if (R == 0) {
+        if (lg == 0) s_red[w * 64 + col] = am;
+      } else {
+        // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
+        const uint32_t code = ue8m0_for_amax(am);
+        const int ex = 127 - (int)code;
+        const bool valid = col < cnt;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint32_t q = 0;
+          if (am > 0.f)
+            q = pack_fp8x4(clamp448(ldexpf(v[s][i][0], ex)), clamp448(ldexpf(v[s][i][1], ex)),
+                           clamp448(ldexpf(v[s][i][2], ex)), clamp448(ldexpf(v[s][i][3], ex)));
+          if (valid)
+            *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
+        }
+        if (valid && lg == 0)
+          static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + w] = (uint8_t)code;
       }
-    am = fmaxf(am, __shfl_xor(am, 16, 64));
-    am = fmaxf(am, __shfl_xor(am, 32, 64));
-    if (R == 0) {
-      if (lg == 0) s_red[w * 64 + col] = am;
-    } else {
-      // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
-      const uint32_t code = ue8m0_for_amax(am);
-      const int ex = 127 - (int)code;
-      const bool valid = col < cnt;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint32_t q = 0;
-        if (am > 0.f)
-          q = pack_fp8x4(clamp448(ldexpf(v[s][i][0], ex)), clamp448(ldexpf(v[s][i][1], ex)),
-                         clamp448(ldexpf(v[s][i][2], ex)), clamp448(ldexpf(v[s][i][3], ex)));
-        if (valid)
-          *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
-      }
-      if (valid && lg == 0)
-        static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + w] = (uint8_t)code;
     }
-  }
+  };
+  if (a.precise_silu) swiglu_pass(BoolC<true>{});
+  else swiglu_pass(BoolC<false>{});
   if (R == 0) {
     __syncthreads();
 #pragma unroll

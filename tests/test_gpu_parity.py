@@ -99,6 +99,23 @@ def test_mxfp4_every_tile_size():
     _full_check(spec, _custom(spec, idx=idx))
 
 
+LIMITS = {
+    # the largest expert count and top-k the library takes (LDS arrays of the route kernels)
+    "max_experts_topk": synth.Spec(16, 128, 128, 8192, 64, seed=126, weight_set=126),
+    # the largest hidden size: 128 K blocks in L1, the whole LDS weight-scale staging
+    "max_hidden": synth.Spec(24, 16384, 128, 3, 2, seed=127, weight_set=127),
+    "max_hidden_mxfp4": synth.Spec(24, 16384, 128, 3, 2, recipe=1, seed=128, weight_set=128),
+    # the largest intermediate size: 128 L1 slabs, 128 K blocks in L2
+    "max_intermediate": synth.Spec(24, 128, 16384, 3, 2, seed=129, weight_set=129),
+}
+
+
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_size_limits_full_parity(name):
+    spec = LIMITS[name]
+    _full_check(spec, synth.make_problem(spec))
+
+
 def test_all_tokens_on_one_expert():
     spec = synth.Spec(150, 512, 256, 8, 1, seed=110, weight_set=110)
     _full_check(spec, _custom(spec, idx=np.full((150, 1), 5)))

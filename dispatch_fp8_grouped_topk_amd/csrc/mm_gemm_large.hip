@@ -1,5 +1,5 @@
-// Large-M grouped GEMMs: experts holding more than 64 pool rows (mid-size and prefill
-// batches), where one weight slab is reused by many token rows.
+// Large-M grouped GEMMs, the default for every expert (a tile of one to 256 pool rows), and the
+// four-wave kernel for the L2 GEMM of small MXFP4 tiles (end of file).
 //
 // Orientation as in the small-M kernels (weight rows = MFMA M side, tokens = N side) and the
 // same slab decomposition (L1: one expert x one 128-channel slab, i.e. 256 w1 rows, gate and up;
@@ -13,12 +13,14 @@
 // column groups per wave (1..8), so a ragged tile costs at most one padded group per wave.
 //
 // Both operands and their scales are staged through LDS with LDS-direct buffer loads (no
-// VGPRs in flight), in a ring of 128-K blocks as deep as LDS allows for the tile shape (four
-// blocks for one column group per wave, two for the largest FP8 tiles): while block kb is
-// multiplied, blocks kb+1 .. kb+depth-1 are in flight.  16-byte chunk c of an
+// VGPRs in flight), in rings of 128-K blocks as deep as LDS allows for the tile shape (see
+// Ring: four blocks for one column group per wave, a three-deep weight ring beside a two-deep
+// token ring for FP8 tiles of 5-7 groups, two for the largest FP8 tiles): while block kb is
+// multiplied, the later blocks are in flight.  16-byte chunk c of an
 // FP8 row r sits at slot c ^ ((r >> 1) & 7) (FP4 rows of 64 bytes: c ^ ((r >> 2) & 3)): an
 // operand read serves 16 lanes (16 consecutive rows, one chunk each) per cycle of the 64 LDS
-// banks, and this swizzle puts their chunks in 16 different 16-byte bank groups.  FP8 recipe: each MFMA covers exactly one 128-K scale
+// banks, and this swizzle puts their chunks in 16 different 16-byte bank groups.  FP8 recipe:
+// each MFMA covers exactly one 128-K scale
 // block and is promoted into the float accumulators with (activation scale x weight scale)
 // one column group later, off the MFMA's critical path.  MXFP4 recipe: the UE8M0 scales go to
 // the MFMA, which accumulates directly.
@@ -706,7 +708,7 @@ template <int R, bool L1>
 __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   __shared__ __attribute__((aligned(1024))) Lds L;
   const int n_slabs = L1 ? a.I / kL1SlabCh : (a.H + kWRows - 1) / kWRows;
-  // with the four-wave kernel on, the MXFP4 L2 tiles from hdr[kHdrTilesQuad] on are its
+  // with the four-wave kernel on, the MXFP4 L2 tiles from hdr[kHdrTilesQuad] on are left to it
   const int n_tiles = R == 1 && !L1 && a.quad ? a.hdr[kHdrTilesQuad] : a.hdr[kHdrTilesLarge];
   const int n_items = n_tiles * n_slabs;
   // The item list runs from the costliest tiles (most column groups: MFMA-bound) to the

@@ -31,6 +31,14 @@ __host__ __device__ inline int large_tile_start(int c, int i) {
   const int n = large_tiles(c), g = (c + 15) / 16;
   return 16 * (i * (g / n) + (i < g % n ? i : g % n));
 }
+// Large-M tile-list entry, .x: expert (bits 0-15), rows (bits 16-24), bit 30 set when the tile is
+// its expert's only one (each weight line is then read by exactly one item per slab); .y: the
+// tile's first pool row.
+constexpr int kTileSingle = 1 << 30;
+__host__ __device__ inline int tile_expert(int x) { return x & 0xFFFF; }
+__host__ __device__ inline int tile_rows(int x) { return (x >> 16) & 0x1FF; }
+__host__ __device__ inline bool tile_single(int x) { return (x & kTileSingle) != 0; }
+
 // Column groups per wave of the first (largest) tile of an expert with c > 0 rows: the tile's
 // 16-row groups are shared by two waves.
 __host__ __device__ inline int large_first_ng(int c) {
@@ -71,7 +79,7 @@ struct Args {
   int32_t* pool_src;    // [P]
   float* w_pool;        // [P]
   int2* tiles_s;        // small-M tile list {expert, first pool row}
-  int2* tiles_l;        // large-M tile list {expert | rows << 16, first pool row (absolute)}
+  int2* tiles_l;        // large-M tile list {expert | rows << 16 | kTileSingle, first pool row}
   void* x_sf_pool;      // [H/128][P] words: the x_sf word of each K block of each pool row
   uint8_t* inter_q;     // [P, I]
   void* inter_sf;       // [I/128][P] words: f32 | 4 x UE8M0 (K-major, like x_sf_pool)

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
       for (int i = 0; i < ntl; ++i) {
         const int m0 = large_tile_start(c, i);
         const int m1 = i + 1 < ntl ? large_tile_start(c, i + 1) : c;
-        a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16), carry + inc - c + m0);
+        a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16) | (ntl == 1 ? kTileSingle : 0), carry + inc - c + m0);
       }
     }
     carry += tot;

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void k_combine(Args a) {
       for (int jj = 0; jj < 8; ++jj) {
         v[jj] = v4i{0, 0, 0, 0};
         if (pp[jj] >= 0)                         // masked or invalid slots contribute nothing
-          v[jj] = *reinterpret_cast<const v4i*>(a.slot + ((size_t)t * a.k + j0 + jj) * a.H + n0);
+          v[jj] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(a.slot + ((size_t)t * a.k + j0 + jj) * a.H + n0));
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void k_combine(Args a) {
     v4i o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = (int)(bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16));
-    *reinterpret_cast<v4i*>(a.y + (size_t)t * a.H + n0) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(a.y + (size_t)t * a.H + n0));   // read-once rows, write-once y
   }
 }
 

@@ -14,6 +14,7 @@ on a bounded sample of the same workload.
 """
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -95,6 +96,9 @@ def weight_bytes_per_expert(spec):
     if spec.recipe == 0:
         l1 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
         l2 = H * I + (H // 128) * (I // 128) * 4
+    elif spec.recipe == 2:
+        l1 = 2 * I * H + 2 * I * (H // 32)
+        l2 = H * I + H * (I // 32)
     else:
         l1 = 2 * I * H // 2 + 2 * I * (H // 32)
         l2 = H * I // 2 + H * (I // 32)
@@ -166,6 +170,9 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recipe", type=int, default=None, choices=[0, 1, 2],
+                    help="run the workload's shapes and routing with another weight recipe "
+                         "(2: E4M3 weights with per-32 UE8M0 scales)")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one forward into a HIP graph and time --steps replays "
@@ -188,6 +195,9 @@ def main():
     import synth
 
     spec = synth.CONFIGS[args.config]
+    if args.recipe is not None and args.recipe != spec.recipe:
+        wname = ("FP8 float-128", "MXFP4 weights", "E4M3 weights UE8M0 per 32")[args.recipe]
+        spec = dataclasses.replace(spec, recipe=args.recipe, name=f"{spec.name} ({wname})")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     P = synth.make_weights(spec, dev)
@@ -261,10 +271,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if spec.recipe == 0 else "fp8_e4m3 x fp4_e2m1",
+        "dtype": {0: "fp8_e4m3", 1: "fp8_e4m3 x fp4_e2m1", 2: "fp8_e4m3 (ue8m0 per 32)"}[spec.recipe],
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, quantised to the layer's formats)",
         "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
-                   "recipe": "fp8_b128" if spec.recipe == 0 else "mxfp4w_b32", "routing": spec.routing,
+                   "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
                    "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
         "weight_GBps": round(ab["weights"] / sec / 1e9, 1),
         "tokens_per_s": round(spec.T / sec, 1),

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(HERE, "libmegamoe.so")
 
 RECIPE_FP8_B128 = 0
 RECIPE_MXFP4W_B32 = 1
+RECIPE_MXFP8_B32 = 2
 FLAG_TILE_AUTO = 0
 FLAG_TILE_SMALL = 1
 FLAG_TILE_LARGE = 2
@@ -148,9 +149,10 @@ def expected_shapes(problem: Problem) -> dict:
         return dict(x=(u8, (T, H)), x_sf=(f32, (T, H // 128)), topk_idx=(i32, (T, k)), topk_w=(f32, (T, k)),
                     l1_w=(u8, (E, 2 * I, H)), l1_sf=(f32, (E, 2 * I // 128, H // 128)),
                     l2_w=(u8, (E, H, I)), l2_sf=(f32, (E, H // 128, I // 128)), y=(b16, (T, H)))
+    wk = 1 if problem.recipe == RECIPE_MXFP8_B32 else 2         # K indices per weight byte
     return dict(x=(u8, (T, H)), x_sf=(u8, (T, H // 32)), topk_idx=(i32, (T, k)), topk_w=(f32, (T, k)),
-                l1_w=(u8, (E, 2 * I, H // 2)), l1_sf=(u8, (E, 2 * I, H // 32)),
-                l2_w=(u8, (E, H, I // 2)), l2_sf=(u8, (E, H, I // 32)), y=(b16, (T, H)))
+                l1_w=(u8, (E, 2 * I, H // wk)), l1_sf=(u8, (E, 2 * I, H // 32)),
+                l2_w=(u8, (E, H, I // wk)), l2_sf=(u8, (E, H, I // 32)), y=(b16, (T, H)))
 
 
 NUM_PHASE_EVENTS = 5

@@ -30,7 +30,9 @@ int check_problem(const mega_moe_problem* p) {
   if (p->intermediate <= 0 || p->intermediate % 128 || p->intermediate > 16384) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->num_experts < 1 || p->num_experts > mm::kMaxExperts) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->topk < 1 || p->topk > mm::kMaxTopk) return MEGA_MOE_ERR_INVALID_ARG;
-  if (p->recipe != MEGA_MOE_RECIPE_FP8_B128 && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32) return MEGA_MOE_ERR_INVALID_ARG;
+  if (p->recipe != MEGA_MOE_RECIPE_FP8_B128 && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32 &&
+      p->recipe != MEGA_MOE_RECIPE_MXFP8_B32)
+    return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU))
     return MEGA_MOE_ERR_INVALID_ARG;

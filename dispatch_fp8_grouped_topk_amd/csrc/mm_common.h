@@ -177,6 +177,15 @@ __device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, v4f c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// The per-32 UE8M0 recipes' MFMA: E2M1 weights (recipe 1) or E4M3 weights (recipe 2) as A,
+// E4M3 activations as B, both with their E8M0 scales, accumulating into c.  (The float-scale
+// recipe 0 instantiates it in a branch it never takes.)
+template <int R>
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  if constexpr (R == 1) return mfma_fp4w_fp8(a, b, c, sa, sb);
+  else return mfma_fp8_scaled(a, b, c, sa, sb);
+}
+
 // MFMA 16x16x128 operand layout on gfx950 (measured):
 //  * FP8: lane l carries row (l % 16); its bytes 0..15 are K [16*(l/16), +16) and its
 //    bytes 16..31 are K [64 + 16*(l/16), +16) of the 128-wide K block.

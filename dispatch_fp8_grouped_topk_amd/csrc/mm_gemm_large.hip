@@ -22,8 +22,9 @@
 // banks, and this swizzle puts their chunks in 16 different 16-byte bank groups.  FP8 recipe:
 // each MFMA covers exactly one 128-K scale
 // block and is promoted into the float accumulators with (activation scale x weight scale)
-// one column group later, off the MFMA's critical path.  MXFP4 recipe: the UE8M0 scales go to
-// the MFMA, which accumulates directly.
+// one column group later, off the MFMA's critical path.  Per-32 recipes (E2M1 or E4M3
+// weights): the UE8M0 scales go to the MFMA, which accumulates directly; the E4M3-weight recipe
+// stages its weights exactly as the FP8 recipe does and its scales as the MXFP4 recipe does.
 //
 // The grid is persistent: the workgroups walk the (tile, slab) items in rounds, half of each
 // round from the costly end of the item list and half from the cheap end (see k_large), and
@@ -47,7 +48,7 @@ constexpr int kWRows = 256;                   // weight rows per tile
 // Ring geometry for recipe R and NG column groups per wave.  A stage of block kb has a weight
 // part (the 256 weight rows: 128 bytes of E4M3 or 64 of E2M1 each) and a token part (the first
 // 32 NG token rows, 128 bytes each, and 512 scale words: words [0, 256) are activation scale
-// words in the order (wn, lr, i) of the readers (see tok_scale_row), words [256, 512) the MXFP4
+// words in the order (wn, lr, i) of the readers (see tok_scale_row), words [256, 512) the UE8M0
 // scale words (4 x UE8M0) of weight rows 0..255).  The weight parts and the token parts sit in
 // two rings.  Where three or four whole stages fit in the LDS left beside the per-tile arrays,
 // both rings take that depth; where only two would, the weight ring (streamed from HBM, the
@@ -57,7 +58,7 @@ constexpr int kRingBudget = 160 * 1024 - 3 * 1024 - 256;
 
 template <int R, int NG>
 struct Ring {
-  static constexpr int kWBytes = kWRows * (R == 0 ? 128 : 64);
+  static constexpr int kWBytes = kWRows * (R == 1 ? 64 : 128);
   static constexpr int kXRows = 32 * NG;
   static constexpr int kTBytes = kXRows * 128 + 2048;
   static constexpr int kFit = kRingBudget / (kWBytes + kTBytes);
@@ -156,7 +157,7 @@ __device__ __forceinline__ int scl_w(int row) { return 256 + row; }
 //   scales:  one word per lane: waves 0-3 the activation scale word 64w + lane, from the
 //            K-major pool-order scale array (one K block of the tile's rows is one contiguous
 //            kilobyte: a gather of one word per row costs the address unit about a lane a
-//            cycle), waves 4-7 the MXFP4 scale word of weight row 64(w-4) + lane (FP8: a
+//            cycle), waves 4-7 the UE8M0 scale word of weight row 64(w-4) + lane (FP8: a
 //            filler, the first word of the array, into words nobody reads).
 struct Src {
   rsrc_t wr;                                  // the expert's weight rows
@@ -170,7 +171,7 @@ struct Src {
 };
 
 template <int R>
-constexpr int kWeightLoads = R == 0 ? 4 : 2;
+constexpr int kWeightLoads = R == 1 ? 2 : 4;
 constexpr int kSpreadGroups = 3;              // column groups the stage loads are spread over
 template <int NG>
 constexpr int kTokenLoads = (NG + 1) / 2;
@@ -198,7 +199,7 @@ __device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int 
   const int jt = split ? j : j - NW;                 // index within the token part
   const int jw = split ? j - NT - 1 : j;             // index within the weight part
   if (is_w) {
-    uint8_t* dst = R == 0 ? F.w + (32 * w + 8 * jw) * 128 : F.w + (32 * w + 16 * jw) * 64;
+    uint8_t* dst = R != 1 ? F.w + (32 * w + 8 * jw) * 128 : F.w + (32 * w + 16 * jw) * 64;
     if (NTW) lds_load16_nt(s.wr, s.wo[jw], bw * s.wkb, dst);
     else lds_load16(s.wr, s.wo[jw], bw * s.wkb, dst);
   } else if (jt < NT) {
@@ -270,7 +271,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   const int tsp = tok_scale_pos(wn, lr);
   // lane offsets inside a stage's weight and token tiles
   const int sw7 = (lr >> 1) & 7;
-  const int wlo = R == 0 ? arow0 * 128 + 16 * (lg ^ sw7) : arow0 * 64 + 16 * (lg ^ ((lr >> 2) & 3));
+  const int wlo = R != 1 ? arow0 * 128 + 16 * (lg ^ sw7) : arow0 * 64 + 16 * (lg ^ ((lr >> 2) & 3));
   const int whi = arow0 * 128 + 16 * ((lg | 4) ^ sw7);
   const int xrow0 = 16 * wn + lr;
   const int xlo = xrow0 * 128 + 16 * (lg ^ sw7);
@@ -331,7 +332,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     v8i A[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if (R == 0) A[rt] = lds_fp8_operand(S.w + wlo, S.w + whi, a_tile_rows<L1>(rt) * 128);
+      if (R != 1) A[rt] = lds_fp8_operand(S.w + wlo, S.w + whi, a_tile_rows<L1>(rt) * 128);
       else A[rt] = lds_fp4_operand(S.w + wlo, a_tile_rows<L1>(rt) * 64);
     }
     uint32_t sw8[8];                       // activation scale words of column groups 0..NG-1
@@ -402,7 +403,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
         const int sx = (sw8[i] >> (8 * lg)) & 0xFF;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_fp4w_fp8(A[rt], B, acc[rt][i], swv[rt], sx);
+        for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_mx<R>(A[rt], B, acc[rt][i], swv[rt], sx);
         __builtin_amdgcn_sched_barrier(0);
         fetch_part(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -422,7 +423,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 // Per-lane global offsets of one wave's share of the token rows (tile rows
 // 8 token_block(w, j) + lane/8) and of its scale word.  sf_pool: the K-major activation scales
 // ([KB][P] words; the tile's rows are pool rows off .. off + cnt - 1, padding rows repeat the
-// last); w_sf: the MXFP4 weight scale rows, grow(r) maps a tile row to the weight row within
+// last); w_sf: the UE8M0 weight scale rows, grow(r) maps a tile row to the weight row within
 // the expert.
 template <int R, int NG, class F>
 __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, rsrc_t sf_pool,
@@ -434,14 +435,14 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
     s.xo[j] = (uint32_t)rowsrc[r] * row_bytes + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
   const int d = 64 * (w & 3) + lane;
-  const bool wscale = R == 1 && w >= 4;
+  const bool wscale = R != 0 && w >= 4;
   s.cr = wscale ? w_sf : sf_pool;
   s.ckb = wscale ? 4 : 4 * P;
   if (w < 4) {
     const int r = tok_scale_row(d);
     s.co = 4u * (uint32_t)(off + (r < cnt ? r : cnt - 1));
   } else {
-    s.co = R == 1 ? (uint32_t)grow(d) * wsrow_bytes : 0u;   // FP8: one word, read by every lane
+    s.co = R != 0 ? (uint32_t)grow(d) * wsrow_bytes : 0u;   // FP8: one word, read by every lane
   }
 }
 
@@ -449,7 +450,7 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
 // the weight row within the expert.
 template <int R, class F>
 __device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_bytes, int w, int lane) {
-  if (R == 0) {
+  if (R != 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 32 * w + 8 * j + (lane >> 3);
@@ -474,12 +475,12 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   const int H = a.H, I = a.I, KB = H / 128;
 
   Src src;
-  const size_t wrow_bytes = R == 0 ? (size_t)H : (size_t)H / 2;
-  src.wkb = R == 0 ? 128 : 64;
+  const size_t wrow_bytes = R == 1 ? (size_t)H / 2 : (size_t)H;
+  src.wkb = R == 1 ? 64 : 128;
   src.wr = make_rsrc(a.l1_w + (size_t)e * 2 * I * wrow_bytes, 2 * (size_t)I * wrow_bytes);
   src.xr = make_rsrc(a.x, (size_t)a.T * H);
   const rsrc_t sf_pool = make_rsrc(a.x_sf_pool, (size_t)KB * a.P * 4);
-  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R == 1 ? (size_t)e * 2 * I * (H / 32) : 0),
+  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R != 0 ? (size_t)e * 2 * I * (H / 32) : 0),
                                 2 * (size_t)I * (H / 32));
   // Gate tile row 32 wm + 16 t + m (and the up tile row 128 further on) holds channel
   // 32 wm + 8 (m / 4) + 4 t + m % 4 of the slab: the lane holding rows 4 lg .. 4 lg + 3 of both
@@ -533,7 +534,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
       if (R == 0) {
         if (lg == 0) red[wm][col] = am;
       } else {
-        // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
+        // per-32 recipes: the 32-channel group is this wave's two gate tiles
         const uint32_t code = ue8m0_for_amax(am);
         const int ex = 127 - (int)code;
         const bool valid = col < cnt;
@@ -582,12 +583,12 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   const int H = a.H, I = a.I, KB = I / 128;
 
   Src src;
-  const size_t wrow_bytes = R == 0 ? (size_t)I : (size_t)I / 2;
-  src.wkb = R == 0 ? 128 : 64;
+  const size_t wrow_bytes = R == 1 ? (size_t)I / 2 : (size_t)I;
+  src.wkb = R == 1 ? 64 : 128;
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
   const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
-  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R == 1 ? (size_t)e * H * (I / 32) : 0),
+  const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R != 0 ? (size_t)e * H * (I / 32) : 0),
                                 (size_t)H * (I / 32));
   // Tile row 64 wm + 16 rt + m holds output column 64 wm + 16 (m / 4) + 4 rt + m % 4 of the
   // slab: the lane holding rows 4 lg .. 4 lg + 3 of the four tiles then holds 16 consecutive
@@ -669,7 +670,7 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   // FP8 weight lines of an expert with one tile are read once: stream them non-temporally (L1;
   // in L2 only for tiles of at most 32 rows, the pure weight streams: measured, the hint made the
   // L2 of larger single tiles up to 6% slower while it takes 3-9% off these)
-  const bool nt = R == 0 && tile_single(td.x) && (L1 || cnt <= 32);
+  const bool nt = R != 1 && tile_single(td.x) && (L1 || cnt <= 32);
   if (tid < kTok) {
     const int pr = off + (tid < cnt ? tid : cnt - 1);
     const int src_pair = a.pool_src[pr];
@@ -706,9 +707,9 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   switch (nw) {
 #define MM_CASE(n)                                                                   \
   case n:                                                                            \
-    if (R == 0 && nt) {                                                              \
-      if (L1) l1_large_tile<R, n, R == 0>(a, e, off, cnt, slab, L);                  \
-      else l2_large_tile<R, n, R == 0>(a, e, off, cnt, slab, L);                     \
+    if (R != 1 && nt) {                                                              \
+      if (L1) l1_large_tile<R, n, R != 1>(a, e, off, cnt, slab, L);                  \
+      else l2_large_tile<R, n, R != 1>(a, e, off, cnt, slab, L);                     \
     } else {                                                                         \
       if (L1) l1_large_tile<R, n, false>(a, e, off, cnt, slab, L);                   \
       else l2_large_tile<R, n, false>(a, e, off, cnt, slab, L);                      \
@@ -1018,7 +1019,8 @@ template <bool L1>
 hipError_t launch_large(const Args& a, hipStream_t s) {
   if (a.max_tiles_l == 0 || a.tile_mode == 1) return hipSuccess;
   if (a.recipe == 0) hipLaunchKernelGGL((k_large<0, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_large<1, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  else if (a.recipe == 1) hipLaunchKernelGGL((k_large<1, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_large<2, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
   if constexpr (!L1)
     if (a.recipe == 1 && a.quad) hipLaunchKernelGGL(k_quad_l2, dim3(a.quad_grid), dim3(kQThreads), 0, s, a);
   return hipGetLastError();

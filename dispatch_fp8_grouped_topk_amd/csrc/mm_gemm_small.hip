@@ -11,7 +11,7 @@
 // L1 (design page sections 5.3 and 10.1): a workgroup owns one expert, up to 64 pool rows and
 // one 128-channel slab of the intermediate, i.e. gate rows [128s, 128s+128) and up rows
 // [I+128s, I+128s+128) of w1; the whole re-quantisation group (128 channels for the float
-// recipe, 32 for the UE8M0 recipe) therefore lives inside the workgroup and the SwiGLU, top-k
+// recipe, 32 for the UE8M0 recipes) therefore lives inside the workgroup and the SwiGLU, top-k
 // weight, amax, scale and E4M3 cast are fused after the K loop.
 //
 // L2 (design page section 11.1): a workgroup owns one expert, up to 64 pool rows and 256
@@ -20,8 +20,8 @@
 // FP8 recipe: each 16x16x128 MFMA spans exactly one 128-wide scale block, so its result is
 // promoted into the float32 accumulator with that block's activation x weight scale (the
 // design page's software scale application, one FMA per accumulator element per block).
-// MXFP4 recipe: E2M1 weights and E4M3 activations go through the block-scaled MFMA with their
-// per-32 UE8M0 scales; no promotion is needed.
+// Per-32 recipes: E2M1 (MXFP4) or E4M3 (MXFP8) weights and E4M3 activations go through the
+// block-scaled MFMA with their per-32 UE8M0 scales; no promotion is needed.
 #include "mm_common.h"
 
 namespace mm {
@@ -41,6 +41,9 @@ struct OpLoad<0> {
     return load_fp8_operand(row + 128 * kb, lg);
   }
 };
+// E4M3 weight rows with per-32 UE8M0 scales: laid out as the FP8 recipe's.
+template <>
+struct OpLoad<2> : OpLoad<0> {};
 // E2M1 weight rows: K block kb starts at byte 64*kb.
 template <>
 struct OpLoad<1> {
@@ -74,7 +77,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
   __syncthreads();
 
   // operand rows
-  const size_t wstride = R == 0 ? (size_t)H : (size_t)H / 2;
+  const size_t wstride = R == 1 ? (size_t)H / 2 : (size_t)H;
   const uint8_t* wrow[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -148,7 +151,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
       for (int s = 0; s < NSUB; ++s) {
         const int sx = sfx[(16 * s + lr) * G + 4 * kb + lg];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt][s] = mfma_fp4w_fp8(A[rt], B[s], acc[rt][s], sw[rt], sx);
+        for (int rt = 0; rt < 4; ++rt) acc[rt][s] = mfma_mx<R>(A[rt], B[s], acc[rt][s], sw[rt], sx);
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) A[rt] = An[rt];
@@ -184,7 +187,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
       if (R == 0) {
         if (lg == 0) s_red[w * 64 + col] = am;
       } else {
-        // MXFP4 recipe: the 32-channel group is this wave's two gate tiles
+        // per-32 recipes: the 32-channel group is this wave's two gate tiles
         const uint32_t code = ue8m0_for_amax(am);
         const int ex = 127 - (int)code;
         const bool valid = col < cnt;
@@ -275,7 +278,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
   const int nbase = kL2SlabRows * slab + 64 * w;               // this wave's first output column
   if (nbase >= H) return;                                      // H is a multiple of 128: whole wave out
 
-  const size_t wstride = R == 0 ? (size_t)I : (size_t)I / 2;
+  const size_t wstride = R == 1 ? (size_t)I / 2 : (size_t)I;
   const uint8_t* wrow[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wrow[rt] = a.l2_w + ((size_t)e * H + nbase + 16 * rt + lr) * wstride;
@@ -345,7 +348,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
       for (int s = 0; s < NSUB; ++s) {
         const int sx = sfx[(16 * s + lr) * G + 4 * kb + lg];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt][s] = mfma_fp4w_fp8(A[rt], B[s], acc[rt][s], sw[rt], sx);
+        for (int rt = 0; rt < 4; ++rt) acc[rt][s] = mfma_mx<R>(A[rt], B[s], acc[rt][s], sw[rt], sx);
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) A[rt] = An[rt];
@@ -398,7 +401,8 @@ hipError_t launch_l1_small(const Args& a, hipStream_t s) {
   if (!small_class_used(a)) return hipSuccess;
   const int grid = round8((long)a.max_tiles_s * (a.I / kL1SlabCh));
   if (a.recipe == 0) hipLaunchKernelGGL(k_l1_small<0>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_l1_small<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.recipe == 1) hipLaunchKernelGGL(k_l1_small<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_l1_small<2>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -406,7 +410,8 @@ hipError_t launch_l2_small(const Args& a, hipStream_t s) {
   if (!small_class_used(a)) return hipSuccess;
   const int grid = round8((long)a.max_tiles_s * ((a.H + kL2SlabRows - 1) / kL2SlabRows));
   if (a.recipe == 0) hipLaunchKernelGGL(k_l2_small<0>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_l2_small<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.recipe == 1) hipLaunchKernelGGL(k_l2_small<1>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_l2_small<2>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

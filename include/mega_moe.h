@@ -29,14 +29,20 @@
  *                              32 channels; w1, w2 are E2M1 nibbles (two per byte, low
  *                              nibble = even K index) with a UE8M0 scale per (row, 32 K).
  *                              (PR #411 "SM90 FP8 x MXFP4 MegaMoE"; UE8M0 = 2^(code-127).)
+ *   MEGA_MOE_RECIPE_MXFP8_B32  as MXFP4W_B32, but w1, w2 are E4M3FN bytes (one per K index) with a
+ *                              UE8M0 scale per (row, 32 K): FP8 activations and weights with the
+ *                              SM100 scale format, packed UE8M0 per 32 K for activations, weights
+ *                              and the intermediate (research report "MegaMoE on SM100/SM90",
+ *                              section 8.4, scale-factor formats; design page section 2, the
+ *                              scale-factor row of the SM100/SM90 comparison).
  *
  * Layouts (all row-major, contiguous, device memory):
- *   x        u8  [T, H]                     x_sf  f32 [T, H/128]  | u8 [T, H/32]
+ *   x        u8  [T, H]                     x_sf  f32 [T, H/128]  | u8 [T, H/32]  (per-32 recipes)
  *   topk_idx i32 [T, k]                     topk_w f32 [T, k]
- *   l1_w     u8  [E, 2I, H]  | [E, 2I, H/2] rows 0..I-1 gate, I..2I-1 up
- *   l1_sf    f32 [E, 2I/128, H/128]         | u8 [E, 2I, H/32]
- *   l2_w     u8  [E, H, I]   | [E, H, I/2]
- *   l2_sf    f32 [E, H/128, I/128]          | u8 [E, H, I/32]
+ *   l1_w     u8  [E, 2I, H]  | [E, 2I, H/2] rows 0..I-1 gate, I..2I-1 up   (MXFP8: [E, 2I, H])
+ *   l1_sf    f32 [E, 2I/128, H/128]         | u8 [E, 2I, H/32]            (MXFP8: as MXFP4)
+ *   l2_w     u8  [E, H, I]   | [E, H, I/2]                                 (MXFP8: [E, H, I])
+ *   l2_sf    f32 [E, H/128, I/128]          | u8 [E, H, I/32]             (MXFP8: as MXFP4)
  *   y        bf16 (u16 bits) [T, H]
  * Every pointer must be 16-byte aligned.  Ids < 0 in topk_idx mark masked slots; ids
  * >= E are dropped (contribute nothing) and counted in the num_invalid view.
@@ -67,7 +73,8 @@ extern "C" {
 
 typedef enum {
   MEGA_MOE_RECIPE_FP8_B128 = 0,
-  MEGA_MOE_RECIPE_MXFP4W_B32 = 1
+  MEGA_MOE_RECIPE_MXFP4W_B32 = 1,
+  MEGA_MOE_RECIPE_MXFP8_B32 = 2
 } mega_moe_recipe;
 
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from

@@ -19,7 +19,11 @@ What it computes, step by step, with where the pages define each step:
    Application", and section 15.2 for the weight-scale layout):
    acc[p, n] = sum over K blocks kb of sfa[t, kb] * sfb[e, n/128, kb] *
    (sum over k in kb of a[t, k] * b[e, n, k]).  The FP8 x MXFP4 recipe uses
-   32-wide K blocks with power-of-two scales on both operands (PR #411).
+   32-wide K blocks with power-of-two scales on both operands (PR #411); the
+   FP8 x FP8 per-32 recipe does the same with E4M3 weights, the SM100 scale
+   format (UE8M0 per 32 K for activations, weights and the intermediate: the
+   research report, section 8.4 on scale-factor formats; the design page,
+   section 2, scale-factor row of the architecture-gap table).
 3. SwiGLU epilogue (design page section 10.1 "Register-Based Flow"):
    s = silu(gate) * up with gate = acc[:, :I], up = acc[:, I:]; optionally
    clamped (s to [-c, c], or, as in step 3 of that section, gate and up to
@@ -27,7 +31,8 @@ What it computes, step by step, with where the pages define each step:
    re-quantisation.
 4. Re-quantisation per group of G output channels: amax, float scale
    amax/448 and an E4M3 cast of value/scale (design section 10.1 steps 4-5,
-   G = 128), or a power-of-two UE8M0 scale per 32 channels for the MXFP4 recipe.
+   G = 128), or a power-of-two UE8M0 scale per 32 channels for the two per-32
+   recipes.
 5. L2 block-scaled GEMM over the intermediate (same form as step 2), each
    row's FP32 result cast to BF16 (design page section 11.1).
 6. Combine (design page section 11.2, "Combine Reduce"): per token, the BF16
@@ -50,6 +55,7 @@ from . import codecs as C
 
 RECIPE_FP8_B128 = 0      # E4M3 everywhere, float scales per 128 (x: per token row; w: 128x128)
 RECIPE_MXFP4W_B32 = 1    # E4M3 activations, E2M1 weights, UE8M0 scales per 32 along K
+RECIPE_MXFP8_B32 = 2     # E4M3 activations and weights, UE8M0 scales per 32 along K
 
 
 @dataclass(frozen=True)
@@ -109,9 +115,9 @@ def _act_scales(prob: Problem, sf_rows: np.ndarray) -> np.ndarray:
 
 
 def _weight_values(prob: Problem, w: np.ndarray) -> np.ndarray:
-    if prob.recipe == RECIPE_FP8_B128:
-        return C.e4m3_decode(w)
-    return C.e2m1_unpack_decode(w)
+    if prob.recipe == RECIPE_MXFP4W_B32:
+        return C.e2m1_unpack_decode(w)
+    return C.e4m3_decode(w)
 
 
 def _weight_scales_rows(prob: Problem, sf: np.ndarray, n_rows: int) -> np.ndarray:

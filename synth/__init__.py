@@ -35,6 +35,7 @@ FP4_MAX = 6.0
 
 RECIPE_FP8 = 0
 RECIPE_MXFP4 = 1
+RECIPE_MXFP8 = 2       # E4M3 weights with a UE8M0 scale per (row, 32 K); activations as MXFP4's
 
 
 @dataclass(frozen=True)
@@ -163,6 +164,10 @@ def quant_weight(wf: torch.Tensor, recipe: int):
         codes = _fp8_codes(g / sf[:, None, :, None]).view(N, K)
         return codes, sf
     g = wf.view(N, K // 32, 32)
+    if recipe == RECIPE_MXFP8:
+        code = _pow2_code(g.abs().amax(dim=2), FP8_MAX)
+        scale = torch.exp2(code.float() - 127)
+        return _fp8_codes(g / scale[..., None]).view(N, K).contiguous(), code
     code = _pow2_code(g.abs().amax(dim=2), FP4_MAX)
     scale = torch.exp2(code.float() - 127)
     codes = _fp4_codes(g / scale[..., None]).view(N, K)
@@ -179,6 +184,9 @@ def weight_shapes(spec: Spec):
     if spec.recipe == RECIPE_FP8:
         return dict(l1_w=((E, 2 * I, H), torch.uint8), l1_sf=((E, 2 * I // 128, H // 128), torch.float32),
                     l2_w=((E, H, I), torch.uint8), l2_sf=((E, H // 128, I // 128), torch.float32))
+    if spec.recipe == RECIPE_MXFP8:
+        return dict(l1_w=((E, 2 * I, H), torch.uint8), l1_sf=((E, 2 * I, H // 32), torch.uint8),
+                    l2_w=((E, H, I), torch.uint8), l2_sf=((E, H, I // 32), torch.uint8))
     return dict(l1_w=((E, 2 * I, H // 2), torch.uint8), l1_sf=((E, 2 * I, H // 32), torch.uint8),
                 l2_w=((E, H, I // 2), torch.uint8), l2_sf=((E, H, I // 32), torch.uint8))
 

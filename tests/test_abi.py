@@ -55,10 +55,12 @@ def test_workspace_size_grows_with_tokens_and_covers_buffers():
     s4 = mm.mega_moe_workspace_size(_p(T=4096, E=257, k=9, recipe=1))
     assert s4 >= 4096 * 9 * (7168 * 2 + 2048 + 2048 // 32)
     assert mm.mega_moe_workspace_size(_p(T=0)) > 0
+    # the E4M3-weight per-32 recipe keeps the MXFP4 recipe's UE8M0 intermediate scales
+    assert mm.mega_moe_workspace_size(_p(T=4096, E=257, k=9, recipe=2)) == s4
 
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
-                                dict(k=65), dict(recipe=2), dict(clamp=-1.0), dict(clamp=float("nan")),
+                                dict(k=65), dict(recipe=3), dict(recipe=-1), dict(clamp=-1.0), dict(clamp=float("nan")),
                                 dict(flags=16), dict(flags=3), dict(flags=15), dict(T=-1), dict(H=32768)])
 def test_invalid_problem_rejected(kw):
     with pytest.raises(mm.MegaMoEError) as ei:

@@ -21,6 +21,7 @@ CASES = {
     "zipf_fp8_multi_tile": synth.Spec(512, 512, 384, 32, 4, routing="zipf", seed=120, weight_set=120),
     "mxfp4_shared": synth.Spec(160, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=121,
                                weight_set=121),
+    "mxfp8_zipf": synth.Spec(512, 512, 384, 32, 4, recipe=2, routing="zipf", seed=124, weight_set=124),
 }
 
 

@@ -5,6 +5,7 @@ intermediate code); the benchmark-size workloads are compared on sampled tokens,
 dispatch metadata still checked in full.
 """
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -57,6 +58,14 @@ SMALL = {
                                seed=122, weight_set=122),
     "mxfp4_clamp_inputs": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.3, clamp_inputs=True,
                                      seed=123, weight_set=123),
+    # E4M3 weights with per-32 UE8M0 scales (recipe 2): shared expert, multi-tile experts, every
+    # column-group class under Zipf routing, and both clamp readings
+    "mxfp8": synth.Spec(40, 512, 256, 9, 5, recipe=2, routing="uniform_shared", seed=130, weight_set=130),
+    "mxfp8_multi_tile": synth.Spec(300, 512, 384, 4, 2, recipe=2, seed=131, weight_set=131),
+    "mxfp8_zipf_clamp_inputs": synth.Spec(512, 640, 384, 32, 4, recipe=2, routing="zipf", swiglu_clamp=0.3,
+                                          clamp_inputs=True, seed=132, weight_set=132),
+    "mxfp8_clamp": synth.Spec(64, 512, 256, 8, 4, recipe=2, routing="biased", swiglu_clamp=0.05, seed=133,
+                              weight_set=133),
     # more than 16384 pairs: dispatch runs 1024 pairs per workgroup; skewed so that experts
     # fill every large-M column-group class
     "wide_dispatch": synth.Spec(2100, 512, 256, 64, 8, routing="zipf", seed=115, weight_set=115),
@@ -70,7 +79,7 @@ def test_small_problem_full_parity(name):
 
 
 @pytest.mark.parametrize("flags", [0, 1, 2], ids=["auto", "small_only", "large_only"])
-@pytest.mark.parametrize("name", ["ragged", "clamp", "mxfp4_clamp", "zipf"])
+@pytest.mark.parametrize("name", ["ragged", "clamp", "mxfp4_clamp", "zipf", "mxfp8_clamp"])
 def test_precise_silu(name, flags):
     """MEGA_MOE_FLAG_PRECISE_SILU (expf and IEEE division): the same bar against the oracle."""
     import dispatch_fp8_grouped_topk_amd as mm
@@ -80,7 +89,7 @@ def test_precise_silu(name, flags):
 
 @pytest.mark.parametrize("flags", [1, 2], ids=["small_only", "large_only"])
 @pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile", "clamp_inputs",
-                                  "mxfp4_clamp_inputs"])
+                                  "mxfp4_clamp_inputs", "mxfp8", "mxfp8_multi_tile", "mxfp8_zipf_clamp_inputs"])
 def test_forced_tile_class(name, flags):
     spec = SMALL[name]
     _full_check(spec, synth.make_problem(spec), flags)
@@ -105,6 +114,7 @@ LIMITS = {
     # the largest hidden size: 128 K blocks in L1, the whole LDS weight-scale staging
     "max_hidden": synth.Spec(24, 16384, 128, 3, 2, seed=127, weight_set=127),
     "max_hidden_mxfp4": synth.Spec(24, 16384, 128, 3, 2, recipe=1, seed=128, weight_set=128),
+    "max_hidden_mxfp8": synth.Spec(24, 16384, 128, 3, 2, recipe=2, seed=134, weight_set=134),
     # the largest intermediate size: 128 L1 slabs, 128 K blocks in L2
     "max_intermediate": synth.Spec(24, 128, 16384, 3, 2, seed=129, weight_set=129),
 }
@@ -131,7 +141,7 @@ def test_masked_and_invalid_ids():
     _full_check(spec, _custom(spec, idx=idx))
 
 
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_cumulative_expert_recv_stats(recipe):
     """mega_moe_forward_stats adds each expert's received rows (masked and invalid slots
     excluded) to the caller's array, call after call, and leaves y unchanged."""
@@ -184,7 +194,7 @@ def test_repeatable_and_stale_workspace():
     assert torch.equal(y1, y2) and torch.equal(y1, y3)
 
 
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_power_of_two_topk_weight_scaling_is_bitwise(recipe):
     spec = synth.Spec(64, 512, 256, 8, 3, recipe=recipe, seed=113, weight_set=113)
     _say(f"pow2 scaling {spec}")
@@ -212,9 +222,12 @@ def test_one_hot_weights_equal_selected_slot():
 _DEV_CACHE = {}
 
 
-def _device_problem(cfg):
-    """Benchmark-size inputs generated on the GPU (weights shared between configs 1 and 3)."""
+def _device_problem(cfg, recipe=None):
+    """Benchmark-size inputs generated on the GPU (weights shared between configs 1 and 3);
+    ``recipe`` replaces the workload's weight recipe."""
     spec = synth.CONFIGS[cfg]
+    if recipe is not None:
+        spec = replace(spec, recipe=recipe, name=f"{spec.name} recipe {recipe}")
     key = (spec.weight_set, spec.H, spec.I, spec.E, spec.recipe)
     if key not in _DEV_CACHE:
         _DEV_CACHE.clear()
@@ -247,3 +260,18 @@ def test_benchmark_config_sampled_parity(cfg):
     assert_intermediate_close(spec, views, ref)
     rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
     _say(f"config {cfg}: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_mxfp8_benchmark_size_sampled_parity(cfg):
+    """The decode and prefill shapes and routing with E4M3 weights and per-32 UE8M0 scales."""
+    spec, P = _device_problem(cfg, recipe=2)
+    _say(f"config {cfg} recipe 2: {spec.name}")
+    y, views, _ = run_gpu(spec, P)
+    idx = P["topk_idx"].cpu().numpy()
+    assert_dispatch_exact(spec, idx, views)
+    toks = _sample_tokens(spec, idx)
+    ref = run_oracle(spec, P, tokens=toks)
+    assert_intermediate_close(spec, views, ref)
+    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
+    _say(f"config {cfg} recipe 2: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")

@@ -62,7 +62,7 @@ def _nearest_fp8(r):
 
 
 def _row_vals_w(spec, w_row):
-    if spec.recipe == 0:
+    if spec.recipe != 1:                            # E4M3 weight bytes (recipes 0 and 2)
         return [_FP8[b] for b in w_row]
     out = []
     for b in w_row:
@@ -157,6 +157,9 @@ BRUTE_SPECS = {
     "fp8_clamp_inputs": synth.Spec(3, 256, 128, 3, 2, seed=15, weight_set=15, swiglu_clamp=0.2, clamp_inputs=True),
     "mxfp4_clamp_inputs": synth.Spec(3, 256, 128, 3, 2, recipe=1, seed=16, weight_set=16, swiglu_clamp=0.2,
                                      clamp_inputs=True),
+    "mxfp8": synth.Spec(3, 256, 128, 3, 2, recipe=2, seed=18, weight_set=18),
+    "mxfp8_shared_clamp": synth.Spec(2, 128, 64, 3, 2, recipe=2, routing="uniform_shared", seed=19,
+                                     weight_set=19, swiglu_clamp=0.01),
 }
 
 
@@ -182,7 +185,7 @@ def test_oracle_equals_brute_force(name):
 
 
 # ----------------------------------------------------------------------------- library special cases
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_l1_dense_special_case_matches_matmul(recipe):
     spec = synth.Spec(7, 512, 256, 1, 1, recipe=recipe, seed=21, weight_set=21)
     P = _np(synth.make_problem(spec))
@@ -200,6 +203,8 @@ def test_l1_dense_special_case_matches_matmul(recipe):
         pk = torch.from_numpy(P["l1_w"][0]).long()
         w = torch.stack([lut[pk & 15], lut[pk >> 4]], dim=-1).reshape(pk.shape[0], -1)
         ws = torch.exp2(torch.from_numpy(P["l1_sf"][0]).double() - 127).repeat_interleave(32, dim=1)
+    if recipe == 2:
+        w = torch.from_numpy(P["l1_w"][0]).view(torch.float8_e4m3fn).double()
     ref = torch.matmul(x * xs, (w * ws).T).numpy()
     np.testing.assert_allclose(r["l1_acc"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
@@ -236,7 +241,7 @@ def test_input_clamp_applies_to_gate_and_up():
     assert got[0, 0] > 10.0
 
 
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_input_clamp_above_every_accumulator_changes_nothing(recipe):
     spec = synth.Spec(6, 512, 256, 5, 2, recipe=recipe, seed=17, weight_set=17)
     P = _np(synth.make_problem(spec))
@@ -249,7 +254,7 @@ def test_input_clamp_above_every_accumulator_changes_nothing(recipe):
 
 
 # ----------------------------------------------------------------------------- re-quantisation
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_requant_invariants(recipe):
     rng = np.random.default_rng(4)
     prob = oracle.Problem(1, 128, 256, 1, 1, recipe=recipe)
@@ -296,7 +301,7 @@ def test_power_of_two_weight_scaling_is_exact(spec):
         assert np.array_equal(oracle.bf16_bits_to_f32(got["y"]).astype(np.float64), yb)
 
 
-@pytest.mark.parametrize("recipe", [0, 1])
+@pytest.mark.parametrize("recipe", [0, 1, 2])
 def test_one_hot_weights_select_one_expert(recipe):
     spec = synth.Spec(8, 512, 256, 8, 3, recipe=recipe, seed=41, weight_set=41)
     P = _np(synth.make_problem(spec))

@@ -173,6 +173,9 @@ def main():
     ap.add_argument("--recipe", type=int, default=None, choices=[0, 1, 2],
                     help="run the workload's shapes and routing with another weight recipe "
                          "(2: E4M3 weights with per-32 UE8M0 scales)")
+    ap.add_argument("--rowmajor-sf", action="store_true",
+                    help="per-32 recipes: pass the weight scales in their row-major input layout instead of "
+                         "the K-major copy the one-time weight-scale transform writes at load time")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one forward into a HIP graph and time --steps replays "
@@ -204,11 +207,17 @@ def main():
     idx, w = synth.make_routing(spec)
     x, x_sf = synth.make_activations(spec, dev)
     P.update(x=x, x_sf=x_sf, topk_idx=idx.to(dev), topk_w=w.to(dev))
-    prob = mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, args.flags)
+    kmajor_sf = spec.recipe != 0 and not args.rowmajor_sf
+    flags = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if kmajor_sf else 0)
+    prob = mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, flags)
     ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device=dev)
     y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], P["l1_sf"], P["l2_w"], P["l2_sf"], y, ws)
+    l1_sf, l2_sf = P["l1_sf"], P["l2_sf"]
+    if kmajor_sf:        # the weight-load-time transform, outside the timed region
+        l1_sf, l2_sf = mm.mega_moe_transform_weight_scales(prob, l1_sf, l2_sf, stream=stream)
+        torch.cuda.synchronize()
+    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], l1_sf, P["l2_w"], l2_sf, y, ws)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -275,6 +284,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, quantised to the layer's formats)",
         "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
                    "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
+                   "weight_sf": "float-128" if spec.recipe == 0 else ("k-major" if kmajor_sf else "row-major"),
                    "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
         "weight_GBps": round(ab["weights"] / sec / 1e9, 1),
         "tokens_per_s": round(spec.T / sec, 1),

@@ -31,6 +31,7 @@ FLAG_TILE_SMALL = 1
 FLAG_TILE_LARGE = 2
 FLAG_CLAMP_INPUTS = 4   # with swiglu_clamp > 0: clamp gate and up before SiLU
 FLAG_PRECISE_SILU = 8   # SiLU with expf and IEEE division instead of the hardware exp / rcp
+FLAG_WEIGHT_SF_KMAJOR = 16   # per-32 recipes: weight scales from mega_moe_transform_weight_scales
 
 ABI_VERSION = 1
 
@@ -93,6 +94,8 @@ def _load():
     lib.mega_moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mega_moe_forward_stats.restype = ctypes.c_int
     lib.mega_moe_forward_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.mega_moe_transform_weight_scales.restype = ctypes.c_int
+    lib.mega_moe_transform_weight_scales.argtypes = [P, vp, vp, vp, vp, vp]
     lib.mega_moe_forward_profiled.restype = ctypes.c_int
     lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -150,12 +153,43 @@ def expected_shapes(problem: Problem) -> dict:
                     l1_w=(u8, (E, 2 * I, H)), l1_sf=(f32, (E, 2 * I // 128, H // 128)),
                     l2_w=(u8, (E, H, I)), l2_sf=(f32, (E, H // 128, I // 128)), y=(b16, (T, H)))
     wk = 1 if problem.recipe == RECIPE_MXFP8_B32 else 2         # K indices per weight byte
+    if problem.flags & FLAG_WEIGHT_SF_KMAJOR:
+        sf1, sf2 = (E, H // 128, 2 * I, 4), (E, I // 128, H, 4)
+    else:
+        sf1, sf2 = (E, 2 * I, H // 32), (E, H, I // 32)
     return dict(x=(u8, (T, H)), x_sf=(u8, (T, H // 32)), topk_idx=(i32, (T, k)), topk_w=(f32, (T, k)),
-                l1_w=(u8, (E, 2 * I, H // wk)), l1_sf=(u8, (E, 2 * I, H // 32)),
-                l2_w=(u8, (E, H, I // wk)), l2_sf=(u8, (E, H, I // 32)), y=(b16, (T, H)))
+                l1_w=(u8, (E, 2 * I, H // wk)), l1_sf=(u8, sf1),
+                l2_w=(u8, (E, H, I // wk)), l2_sf=(u8, sf2), y=(b16, (T, H)))
 
 
 NUM_PHASE_EVENTS = 5
+
+
+def mega_moe_transform_weight_scales(problem: Problem, l1_sf, l2_sf, stream=None):
+    """The per-32 recipes' one-time weight-scale transform: returns new K-major tensors
+    (l1 [E, H/128, 2I, 4], l2 [E, I/128, H, 4] uint8) for forward calls whose problem has
+    FLAG_WEIGHT_SF_KMAJOR set."""
+    import torch
+    dev = l1_sf.device
+    if dev.type != "cuda":
+        raise ValueError("mega_moe_transform_weight_scales needs device tensors")
+    rowmajor = Problem.make(problem.num_tokens, problem.hidden, problem.intermediate, problem.num_experts,
+                            problem.topk, problem.recipe, problem.swiglu_clamp,
+                            problem.flags & ~FLAG_WEIGHT_SF_KMAJOR)
+    shapes = expected_shapes(rowmajor)
+    for name, t in (("l1_sf", l1_sf), ("l2_sf", l2_sf)):
+        _check_tensor(name, t, dev, *shapes[name])
+    E, H, I = problem.num_experts, problem.hidden, problem.intermediate
+    out1 = torch.empty(E, H // 128, 2 * I, 4, dtype=torch.uint8, device=dev)
+    out2 = torch.empty(E, I // 128, H, 4, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _load().mega_moe_transform_weight_scales(ctypes.byref(rowmajor), _ptr(l1_sf), _ptr(l2_sf), _ptr(out1),
+                                                  _ptr(out2), ctypes.c_void_p(handle))
+    if st:
+        raise MegaMoEError(st, "mega_moe_transform_weight_scales")
+    return out1, out2
 
 
 def mega_moe_forward(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,

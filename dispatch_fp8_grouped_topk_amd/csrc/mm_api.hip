@@ -34,7 +34,11 @@ int check_problem(const mega_moe_problem* p) {
       p->recipe != MEGA_MOE_RECIPE_MXFP8_B32)
     return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
-  if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU))
+  if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU |
+                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  // the K-major weight-scale layout exists for the per-32 (UE8M0) recipes only
+  if ((p->flags & MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR) && p->recipe == MEGA_MOE_RECIPE_FP8_B128)
     return MEGA_MOE_ERR_INVALID_ARG;
   if ((p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_MASK) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->num_tokens * (int64_t)p->topk > (int64_t)(INT_MAX / 2)) return MEGA_MOE_ERR_INVALID_ARG;
@@ -203,6 +207,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.clamp = std::isinf(p->swiglu_clamp) ? 0.f : p->swiglu_clamp;
   a.clamp_inputs = (p->flags & MEGA_MOE_FLAG_CLAMP_INPUTS) != 0;
   a.precise_silu = (p->flags & MEGA_MOE_FLAG_PRECISE_SILU) != 0;
+  a.wsf_kmajor = (p->flags & MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR) != 0;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
   a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;
@@ -261,4 +266,36 @@ MM_EXPORT int mega_moe_forward_profiled(const mega_moe_problem* p, const void* x
     if (!events[i]) return MEGA_MOE_ERR_NULL_POINTER;
   return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
                       workspace_bytes, stream, events, num_events, nullptr);
+}
+
+MM_EXPORT int mega_moe_transform_weight_scales(const mega_moe_problem* p, const void* l1_sf, const void* l2_sf,
+                                               void* l1_sf_kmajor, void* l2_sf_kmajor, void* stream) {
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->recipe == MEGA_MOE_RECIPE_FP8_B128) return MEGA_MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {l1_sf, l2_sf, l1_sf_kmajor, l2_sf_kmajor};
+  for (const void* q : ptrs)
+    if (!q) return MEGA_MOE_ERR_NULL_POINTER;
+  for (const void* q : ptrs)
+    if (misaligned(q)) return MEGA_MOE_ERR_MISALIGNED;
+  const int H = p->hidden, I = p->intermediate, E = p->num_experts;
+  // out of place only: neither output may overlap an input or the other output
+  const auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+  };
+  const size_t n1 = (size_t)E * 2 * I * (H / 32), n2 = (size_t)E * H * (I / 32);
+  if (overlap(l1_sf_kmajor, n1, l1_sf, n1) || overlap(l1_sf_kmajor, n1, l2_sf, n2) ||
+      overlap(l2_sf_kmajor, n2, l1_sf, n1) || overlap(l2_sf_kmajor, n2, l2_sf, n2) ||
+      overlap(l1_sf_kmajor, n1, l2_sf_kmajor, n2))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mm::launch_sf_kmajor(static_cast<const uint32_t*>(l1_sf), static_cast<uint32_t*>(l1_sf_kmajor), E, 2 * I,
+                           H / 128, s) != hipSuccess ||
+      mm::launch_sf_kmajor(static_cast<const uint32_t*>(l2_sf), static_cast<uint32_t*>(l2_sf_kmajor), E, H,
+                           I / 128, s) != hipSuccess)
+    return MEGA_MOE_ERR_HIP;
+  return MEGA_MOE_OK;
 }

@@ -96,6 +96,8 @@ struct Args {
   int large_grid;       // workgroups of the persistent large-M kernels (multiple of 8)
   int quad;             // 1: MXFP4 L2 tiles of at most 160 rows go to the four-wave kernel
   int quad_grid;        // its workgroups (two per CU, multiple of 8)
+  int wsf_kmajor;       // per-32 recipes: weight scales as [E][K/128][rows] words (4 UE8M0 codes
+                        // of one 128-K block of one row), else [E][rows][K/32] bytes
 };
 
 // ------------------------------------------------------------------------------------------
@@ -233,4 +235,6 @@ hipError_t launch_l2_small(const Args& a, hipStream_t s);
 hipError_t launch_l1_large(const Args& a, hipStream_t s);
 hipError_t launch_l2_large(const Args& a, hipStream_t s);
 hipError_t launch_combine(const Args& a, hipStream_t s);
+// out[e][kb][r] = in[e][r][kb] over E experts of `rows` rows and KB words per row (32-bit words)
+hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s);
 }  // namespace mm

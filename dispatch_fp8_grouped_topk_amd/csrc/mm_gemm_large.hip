@@ -423,12 +423,14 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 // Per-lane global offsets of one wave's share of the token rows (tile rows
 // 8 token_block(w, j) + lane/8) and of its scale word.  sf_pool: the K-major activation scales
 // ([KB][P] words; the tile's rows are pool rows off .. off + cnt - 1, padding rows repeat the
-// last); w_sf: the UE8M0 weight scale rows, grow(r) maps a tile row to the weight row within
-// the expert.
+// last); w_sf: the expert's UE8M0 weight scales, grow(r) maps a tile row to the weight row within
+// the expert, a row's scale word of K block kb sits at grow(r) * wsrow_bytes + kb * wskb (row-major
+// scales: one row's words are consecutive; K-major: one K block's rows are, so a wave's 64 rows
+// are 256 contiguous bytes instead of 64 cache lines).
 template <int R, int NG, class F>
 __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, rsrc_t sf_pool,
                                               int P, int off, int cnt, rsrc_t w_sf, F grow,
-                                              uint32_t wsrow_bytes, int w, int lane) {
+                                              uint32_t wsrow_bytes, int wskb, int w, int lane) {
 #pragma unroll
   for (int j = 0; j < kTokenLoads<NG>; ++j) {
     const int r = 8 * token_block<NG>(w, j) + (lane >> 3);
@@ -437,7 +439,7 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
   const int d = 64 * (w & 3) + lane;
   const bool wscale = R != 0 && w >= 4;
   s.cr = wscale ? w_sf : sf_pool;
-  s.ckb = wscale ? 4 : 4 * P;
+  s.ckb = wscale ? wskb : 4 * P;
   if (w < 4) {
     const int r = tok_scale_row(d);
     s.co = 4u * (uint32_t)(off + (r < cnt ? r : cnt - 1));
@@ -491,7 +493,8 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
     return (r < 128 ? 0 : I) + 128 * slab + c;
   };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
-  token_offsets<R, NG>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, H / 32, w, lane);
+  token_offsets<R, NG>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : H / 32,
+                       a.wsf_kmajor ? 8 * I : 4, w, lane);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = rt < 2 ? 0 : 1;
@@ -600,7 +603,8 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
     return g < H ? g : g - 128;
   };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
-  token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, I / 32, w, lane);
+  token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : I / 32,
+                       a.wsf_kmajor ? 4 * H : 4, w, lane);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = wm >> 1;
@@ -944,14 +948,14 @@ __device__ __forceinline__ void q_tile(const Args& a, int e, int off, int cnt, i
   src.ar = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
   src.akb = 4 * a.P;
   src.sr = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32), (size_t)H * (I / 32));
-  src.skb = 4;
+  src.skb = a.wsf_kmajor ? 4 * H : 4;           // K-major weight scales: one K block's rows adjacent
   // output-column permutation of the eight-wave kernel (16 consecutive columns per lane)
   const auto grow = [&](int r) {
     const int m = r & 15, rt = (r >> 4) & 3;
     const int g = kWRows * slab + (r & ~63) + 16 * (m >> 2) + 4 * rt + (m & 3);
     return g < H ? g : g - 128;
   };
-  q_offsets<NC>(src, L.rowsrc, I, grow, I / 2, I / 32, off, cnt, w, lane);
+  q_offsets<NC>(src, L.rowsrc, I, grow, I / 2, a.wsf_kmajor ? 4 : I / 32, off, cnt, w, lane);
   v4f acc[4][NC];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)

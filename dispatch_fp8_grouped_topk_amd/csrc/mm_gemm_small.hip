@@ -130,11 +130,13 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
     }
   } else {
     const int G = H / 32;
+    // a row's codes of K block kb: row * rs + kb * ks (row-major or K-major weight scales)
+    const size_t rs = a.wsf_kmajor ? 4 : G, ks = a.wsf_kmajor ? (size_t)8 * I : 4;
     const uint8_t* sfw[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int row = (rt < 2 ? 0 : I) + 128 * slab + 32 * w + 16 * (rt & 1) + lr;
-      sfw[rt] = static_cast<const uint8_t*>(a.l1_sf) + ((size_t)e * 2 * I + row) * G + lg;
+      sfw[rt] = static_cast<const uint8_t*>(a.l1_sf) + (size_t)e * 2 * I * G + row * rs + lg;
     }
     const uint8_t* sfx = s_scale;
     for (int kb = 0; kb < KB; ++kb) {
@@ -146,7 +148,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(xrow[s] + 128 * kn, lg);
       int sw[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) sw[rt] = sfw[rt][4 * kb];
+      for (int rt = 0; rt < 4; ++rt) sw[rt] = sfw[rt][ks * kb];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         const int sx = sfx[(16 * s + lr) * G + 4 * kb + lg];
@@ -329,10 +331,11 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
     }
   } else {
     const int G = I / 32;
+    const size_t rs = a.wsf_kmajor ? 4 : G, ks = a.wsf_kmajor ? (size_t)4 * H : 4;
     const uint8_t* sfw[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
-      sfw[rt] = static_cast<const uint8_t*>(a.l2_sf) + ((size_t)e * H + nbase + 16 * rt + lr) * G + lg;
+      sfw[rt] = static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * G + (nbase + 16 * rt + lr) * rs + lg;
     const uint8_t* sfx = s_scale;
     for (int kb = 0; kb < KB; ++kb) {
       v8i An[4], Bn[NSUB];
@@ -343,7 +346,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(qrow[s] + 128 * kn, lg);
       int sw[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) sw[rt] = sfw[rt][4 * kb];
+      for (int rt = 0; rt < 4; ++rt) sw[rt] = sfw[rt][ks * kb];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         const int sx = sfx[(16 * s + lr) * G + 4 * kb + lg];

@@ -309,4 +309,35 @@ hipError_t launch_combine(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// Weight-scale transform for the per-32 recipes, run once when the weights are loaded (the
+// counterpart of the pages' model-load weight transform, design page section 15, which also
+// re-lays the UE8M0 scale factors out for the kernels' loads): the caller's [E][rows][K/32] codes
+// become [E][K/128][rows] words of four codes, so the GEMMs fetch one K block's scales of 64
+// consecutive rows as 256 contiguous bytes.  A 64-row x 32-word tile per workgroup goes through
+// LDS, so both the reads and the writes are coalesced.
+__global__ __launch_bounds__(256) void k_sf_kmajor(const uint32_t* __restrict__ in, uint32_t* __restrict__ out,
+                                                   int rows, int KB, int row_tiles, int kb_tiles) {
+  __shared__ uint32_t tile[64][33];
+  const int b = blockIdx.x;
+  const int e = b / (row_tiles * kb_tiles), rem = b - e * row_tiles * kb_tiles;
+  const int r0 = 64 * (rem / kb_tiles), k0 = 32 * (rem % kb_tiles);
+  const size_t base = (size_t)e * rows * KB;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;      // 32 x 8
+  for (int r = ty; r < 64; r += 8)
+    if (r0 + r < rows && k0 + tx < KB) tile[r][tx] = in[base + (size_t)(r0 + r) * KB + k0 + tx];
+  __syncthreads();
+  const int ox = threadIdx.x & 63, oy = threadIdx.x >> 6;      // 64 x 4
+  for (int k = oy; k < 32; k += 4)
+    if (r0 + ox < rows && k0 + k < KB) out[base + (size_t)(k0 + k) * rows + r0 + ox] = tile[ox][k];
+}
+
+hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s) {
+  const int row_tiles = (rows + 63) / 64, kb_tiles = (KB + 31) / 32;
+  const long blocks = (long)E * row_tiles * kb_tiles;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sf_kmajor, dim3((unsigned)blocks), dim3(256), 0, s, in, out, rows, KB, row_tiles, kb_tiles);
+  return hipGetLastError();
+}
+
 }  // namespace mm

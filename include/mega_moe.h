@@ -79,8 +79,8 @@ typedef enum {
 
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
-   2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU;
-   other bits must be 0. */
+   2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU,
+   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR; other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
@@ -95,6 +95,11 @@ typedef enum {
  * false, design page section 10.1 step 3); by default the hardware exp and reciprocal
  * instructions (fast_math = true), float32 to a few ulp. */
 #define MEGA_MOE_FLAG_PRECISE_SILU 8u
+/* flags bit 4 (per-32 recipes only; INVALID_ARG with MEGA_MOE_RECIPE_FP8_B128): l1_sf and l2_sf
+ * are in the K-major layout that mega_moe_transform_weight_scales() writes, [E][K/128][rows]
+ * 32-bit words, each the four UE8M0 codes of one row's 128-K block (K = H, rows = 2I for l1_sf;
+ * K = I, rows = H for l2_sf).  Same sizes as the row-major layout; the results are identical. */
+#define MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR 16u
 
 enum {
   MEGA_MOE_OK = 0,
@@ -174,6 +179,19 @@ int mega_moe_forward_stats(const mega_moe_problem* p,
                            const void* l2_w, const void* l2_sf,
                            void* y, void* workspace, size_t workspace_bytes,
                            int32_t* cumulative_expert_recv_stats, void* stream);
+
+/* The per-32 recipes' weight-scale transform, run once when the weights are loaded (the pages'
+   model-load weight transform re-lays the UE8M0 scale factors out for the kernels' loads: design
+   page "MegaMoE SM90 Implementation Design", section 15; research report section 6.2).  Reads the
+   row-major l1_sf [E, 2I, H/32] and l2_sf [E, H, I/32] codes and writes the same codes K-major
+   into l1_sf_kmajor [E, H/128, 2I, 4] and l2_sf_kmajor [E, I/128, H, 4] (caller-allocated, same
+   sizes, distinct from the inputs), for forward calls with MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, whose
+   GEMMs then fetch one K block's scales of 64 consecutive rows as 256 contiguous bytes instead of
+   64 scattered words.  Enqueued on `stream` (a hipStream_t, NULL for the default stream).
+   Errors: INVALID_ARG for the FP8_B128 recipe, an invalid problem or overlapping buffers;
+   NULL_POINTER; MISALIGNED (16 bytes); UNSUPPORTED_DEVICE; HIP. */
+int mega_moe_transform_weight_scales(const mega_moe_problem* p, const void* l1_sf, const void* l2_sf,
+                                     void* l1_sf_kmajor, void* l2_sf_kmajor, void* stream);
 
 /* Fill *out with device pointers into `workspace` for problem p. */
 int mega_moe_workspace_views(const mega_moe_problem* p, const void* workspace,

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import dispatch_fp8_grouped_topk_amd as mm
 
@@ -61,7 +62,7 @@ def test_workspace_size_grows_with_tokens_and_covers_buffers():
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
                                 dict(k=65), dict(recipe=3), dict(recipe=-1), dict(clamp=-1.0), dict(clamp=float("nan")),
-                                dict(flags=16), dict(flags=3), dict(flags=15), dict(T=-1), dict(H=32768)])
+                                dict(flags=32), dict(flags=3), dict(flags=15), dict(flags=16), dict(T=-1), dict(H=32768)])
 def test_invalid_problem_rejected(kw):
     with pytest.raises(mm.MegaMoEError) as ei:
         mm.mega_moe_workspace_size(_p(**kw))
@@ -71,6 +72,39 @@ def test_invalid_problem_rejected(kw):
 def test_numerics_flags_accepted_with_either_tile_class():
     for flags in (4, 5, 6, 8, 12, 14):
         assert mm.mega_moe_workspace_size(_p(clamp=1.0, flags=flags)) > 0
+
+
+def test_weight_sf_kmajor_flag_only_with_per32_recipes():
+    # flag 16 (K-major weight scales) is rejected above for the float-scale recipe
+    for recipe in (1, 2):
+        for flags in (16, 17, 18, 30):
+            assert mm.mega_moe_workspace_size(_p(recipe=recipe, clamp=1.0, flags=flags)) > 0
+
+
+def _transform_raw(problem, ptrs):
+    lib = mm.library()
+    args = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return lib.mega_moe_transform_weight_scales(ctypes.byref(problem), *args, None)
+
+
+def test_transform_weight_scales_validates_before_any_device_work():
+    # small tensors (l1 scales 1 KiB, l2 512 B) at addresses 1 MiB apart never overlap; no address
+    # is dereferenced: every case returns before the device is touched (on a host without a GPU
+    # the valid call stops at the device check)
+    small = dict(T=1, H=128, I=128, E=1, k=1)
+    good = [1 << 20, 2 << 20, 3 << 20, 4 << 20]
+    assert _transform_raw(_p(recipe=0, **small), good) == -1              # float-scale recipe
+    assert _transform_raw(_p(recipe=1, **dict(small, H=100)), good) == -1  # invalid problem
+    for i in range(4):
+        bad = list(good)
+        bad[i] = None
+        assert _transform_raw(_p(recipe=2, **small), bad) == -2
+    assert _transform_raw(_p(recipe=1, **small), [good[0] + 4] + good[1:]) == -3
+    # in place (output overlapping its input) is rejected, out of place gets past validation
+    assert _transform_raw(_p(recipe=2, **small), [good[0], good[1], good[0] + 512, good[3]]) == -1
+    assert _transform_raw(_p(recipe=2, **small), [good[0], good[1], good[1] + 256, good[3]]) == -1
+    if not torch.cuda.is_available():
+        assert _transform_raw(_p(recipe=2, **small), good) in (-5, -6)   # no device to run on
 
 
 def _forward_raw(problem, ptrs, ws_bytes):

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from harness import (assert_dispatch_exact, assert_intermediate_close, assert_y_close, run_gpu,
+from harness import (assert_dispatch_exact, assert_intermediate_close, assert_y_close, problem_of, run_gpu,
                      run_oracle, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -95,9 +95,11 @@ def test_forced_tile_class(name, flags):
     _full_check(spec, synth.make_problem(spec), flags)
 
 
-def test_mxfp4_every_tile_size():
+@pytest.mark.parametrize("flags", [0, 16], ids=["rowmajor_sf", "kmajor_sf"])
+def test_mxfp4_every_tile_size(flags):
     """MXFP4 experts of 1 to 10 row groups of 16 (the four-wave L2 kernel's tile sizes) beside a
-    601-row expert (three tiles of the eight-wave kernel), compared in full."""
+    601-row expert (three tiles of the eight-wave kernel), compared in full, with the weight scales
+    in either layout."""
     counts = [1, 17, 33, 49, 65, 81, 97, 113, 129, 150, 160, 601]
     T, k = sum(counts) // 2, 2
     ids = np.repeat(np.arange(len(counts)), counts)           # sorted; no expert holds T pairs
@@ -105,7 +107,35 @@ def test_mxfp4_every_tile_size():
     idx = idx[np.random.default_rng(117).permutation(T)].astype(np.int32)
     assert (idx[:, 0] != idx[:, 1]).all()
     spec = synth.Spec(T, 512, 256, len(counts), k, recipe=1, seed=117, weight_set=117)
-    _full_check(spec, _custom(spec, idx=idx))
+    _full_check(spec, _custom(spec, idx=idx), flags)
+
+
+# ------------------------------------------------------------------------------ K-major weight scales
+@pytest.mark.parametrize("flags", [0, 1, 2], ids=["auto", "small_only", "large_only"])
+@pytest.mark.parametrize("name", ["mxfp4", "mxfp4_multi_tile", "mxfp4_clamp_inputs", "mxfp8", "mxfp8_multi_tile",
+                                  "mxfp8_zipf_clamp_inputs"])
+def test_weight_sf_kmajor(name, flags):
+    """Weight scales transformed once (mega_moe_transform_weight_scales) and read K-major
+    (MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR): the same bar against the oracle, which reads the originals."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    spec = SMALL[name]
+    _full_check(spec, synth.make_problem(spec), flags | mm.FLAG_WEIGHT_SF_KMAJOR)
+
+
+@pytest.mark.parametrize("recipe", [1, 2])
+def test_weight_sf_transform_is_a_transpose(recipe):
+    """The transform writes [E, K/128, rows, 4] with the codes of [E, rows, K/32], bit for bit
+    (K blocks 5 and 34: one and two 32-word tiles of the transform)."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    for H, I, E in ((640, 384, 5), (4352, 128, 2)):
+        spec = synth.Spec(8, H, I, E, 2, recipe=recipe, seed=135, weight_set=135)
+        _say(f"transform {spec}")
+        D = to_device(synth.make_problem(spec))
+        k1, k2 = mm.mega_moe_transform_weight_scales(problem_of(spec), D["l1_sf"], D["l2_sf"])
+        torch.cuda.synchronize()
+        e1 = D["l1_sf"].view(E, 2 * I, H // 128, 4).permute(0, 2, 1, 3).contiguous()
+        e2 = D["l2_sf"].view(E, H, I // 128, 4).permute(0, 2, 1, 3).contiguous()
+        assert torch.equal(k1, e1) and torch.equal(k2, e2)
 
 
 LIMITS = {
@@ -275,3 +305,19 @@ def test_mxfp8_benchmark_size_sampled_parity(cfg):
     assert_intermediate_close(spec, views, ref)
     rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
     _say(f"config {cfg} recipe 2: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
+
+
+@pytest.mark.parametrize("cfg,recipe", [(4, None), (3, 2)], ids=["mxfp4_c4", "mxfp8_prefill"])
+def test_weight_sf_kmajor_benchmark_size_sampled_parity(cfg, recipe):
+    """The benchmark shapes of the per-32 recipes with K-major weight scales."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    spec, P = _device_problem(cfg, recipe=recipe)
+    _say(f"config {cfg} K-major scales: {spec.name}")
+    y, views, _ = run_gpu(spec, P, mm.FLAG_WEIGHT_SF_KMAJOR)
+    idx = P["topk_idx"].cpu().numpy()
+    assert_dispatch_exact(spec, idx, views)
+    toks = _sample_tokens(spec, idx)
+    ref = run_oracle(spec, P, tokens=toks)
+    assert_intermediate_close(spec, views, ref)
+    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
+    _say(f"config {cfg} K-major: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")

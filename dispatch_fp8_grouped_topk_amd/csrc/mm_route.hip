@@ -110,6 +110,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     if (e < E) {
       int run = 0;
       for (int qq = 0; qq < q; ++qq) run += part[qq][el];
+#pragma unroll 8
       for (int b = b_lo; b < b_hi; ++b) {
         const int c = a.blk[(size_t)b * E + e];
         a.blk[(size_t)b * E + e] = run;
@@ -194,13 +195,17 @@ __global__ __launch_bounds__(1024) void k_route_scan(Args a) {
     carry_s += tot_s;
   }
   const int carry_l = s_class_base[0];
+  // ids >= E over all dispatch blocks: every thread sums a strided share of the per-block counts
+  // (independent loads in flight), then one workgroup reduction
+  int inv = 0;
+  for (int b = tid; b < NB; b += 1024) inv += a.blk_inv[b];
+  int iv[1] = {inv}, itot[1];
+  block_scan_1024_n<1>(iv, sh, itot);
   if (tid == 0) {
     a.offset[E] = carry;
     a.hdr[kHdrTilesSmall] = carry_s;
     a.hdr[kHdrTilesLarge] = carry_l;
-    int inv = 0;
-    for (int b = 0; b < NB; ++b) inv += a.blk_inv[b];
-    a.hdr[kHdrInvalid] = inv;
+    a.hdr[kHdrInvalid] = itot[0];
   }
 }
 

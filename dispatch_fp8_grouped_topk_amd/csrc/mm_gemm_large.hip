@@ -167,6 +167,7 @@ struct Src {
   uint32_t xo[4];
   uint32_t co;
   int wkb;                                    // bytes per K block of a weight row
+  uint32_t wend;                              // bytes of the weight buffer (wr's size)
   int ckb;                                    // bytes per K block of this wave's scale source
 };
 
@@ -191,8 +192,11 @@ __device__ __forceinline__ int token_block(int w, int j) {
 // token part (token blocks, then the scale word) of block bt into F.x / F.scl.  With one ring
 // depth (bw == bt) the weights go first; with a deeper weight ring the token part goes first, so
 // that waiting for a block's token part leaves exactly the next block's weight loads in flight.
+// bw >= KB (the steps past the last block): the weight loads take a lane offset at the end of the
+// buffer, so every lane is out of range and reads zeros into the retired slot without touching
+// memory, and they still count as loads, which keeps the number in flight constant.
 template <int R, int NG, bool NTW>
-__device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int bw, int bt, int w, int j) {
+__device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int bw, int bt, int w, int j, int KB) {
   constexpr int NW = kWeightLoads<R>, NT = kTokenLoads<NG>;
   constexpr bool split = Ring<R, NG>::kSplit;
   const bool is_w = split ? j > NT : j < NW;
@@ -200,8 +204,11 @@ __device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int 
   const int jw = split ? j - NT - 1 : j;             // index within the weight part
   if (is_w) {
     uint8_t* dst = R != 1 ? F.w + (32 * w + 8 * jw) * 128 : F.w + (32 * w + 16 * jw) * 64;
-    if (NTW) lds_load16_nt(s.wr, s.wo[jw], bw * s.wkb, dst);
-    else lds_load16(s.wr, s.wo[jw], bw * s.wkb, dst);
+    const bool past = bw >= KB;
+    const uint32_t vo = past ? s.wend : s.wo[jw];
+    const int so = past ? 0 : bw * s.wkb;
+    if (NTW) lds_load16_nt(s.wr, vo, so, dst);
+    else lds_load16(s.wr, vo, so, dst);
   } else if (jt < NT) {
     lds_load16(s.xr, s.xo[jt], bt * 128, F.x + token_block<NG>(w, jt) * 8 * 128);
   } else {
@@ -280,8 +287,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
   // Prologue: the issue of steps -(NSW - 1) .. -1.  Every step issues its loads without a
-  // branch; past the last block they fetch a copy of block KB - 1 into the slot of a retired
-  // block (never read), so the number of loads in flight behind block kb is always kInFlight.
+  // branch; past the last block the weight loads read zeros (a lane offset at the buffer's end:
+  // no memory access) and the token loads a copy of block KB - 1, into the slots of retired blocks
+  // (never read), so the number of loads in flight behind block kb is always kInFlight.
   static_assert(NSW == NST || NSW == NST + 1, "ring depths");
 #pragma unroll
   for (int j = -(NSW - 1); j < 0; ++j) {
@@ -290,7 +298,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
     for (int l = 0; l < kStageLoads<R, NG>; ++l) {
       const bool is_w = Ring<R, NG>::kSplit ? l > kTokenLoads<NG> : l < kWeightLoads<R>;
-      if (is_w || bt >= 0) issue_load<R, NG, NTW>(F, src, min(bw, KB - 1), min(bt < 0 ? 0 : bt, KB - 1), w, l);
+      if (is_w || bt >= 0) issue_load<R, NG, NTW>(F, src, bw, min(bt < 0 ? 0 : bt, KB - 1), w, l, KB);
     }
   }
   int wslot = 0, tslot = 0;                // weight / token ring slots of block kb
@@ -311,7 +319,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // slots block kb-1 used.  Their loads are issued behind column group 0's MFMAs: issued
     // right after the barrier, every wave's loads queue in the address unit at once and hold
     // the waves back from their first MFMA.
-    const int bw = min(kb + NSW - 1, KB - 1), bt = min(kb + NST - 1, KB - 1);
+    const int bw = kb + NSW - 1, bt = min(kb + NST - 1, KB - 1);
     const int fw = wslot == 0 ? NSW - 1 : wslot - 1, ft = tslot == 0 ? NST - 1 : tslot - 1;
     const StageRef F = stage_ref<R, NG>(L.ring, fw, ft);
     // fetch_part(i) issues the loads due after column group i: all of them after group
@@ -319,7 +327,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // the group loop's schedule.)
     auto fetch_part = [&](int i) {
 #pragma unroll
-      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG, NTW>(F, src, bw, bt, w, j);
+      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG, NTW>(F, src, bw, bt, w, j, KB);
     };
     const StageRef S = stage_ref<R, NG>(L.ring, wslot, tslot);
     wslot = wslot + 1 == NSW ? 0 : wslot + 1;
@@ -415,7 +423,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += pend[rt] * pend_s[rt];
   }
-  // the copies issued past the last block land in retired slots; let them land before the
+  // the loads issued past the last block land in retired slots; let them land before the
   // item ends, so none can reach the LDS once the next item (or kernel) has laid it out anew
   wait_vmcnt<0>();
 }
@@ -480,6 +488,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
   const size_t wrow_bytes = R == 1 ? (size_t)H / 2 : (size_t)H;
   src.wkb = R == 1 ? 64 : 128;
   src.wr = make_rsrc(a.l1_w + (size_t)e * 2 * I * wrow_bytes, 2 * (size_t)I * wrow_bytes);
+  src.wend = (uint32_t)(2 * (size_t)I * wrow_bytes);
   src.xr = make_rsrc(a.x, (size_t)a.T * H);
   const rsrc_t sf_pool = make_rsrc(a.x_sf_pool, (size_t)KB * a.P * 4);
   const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l1_sf) + (R != 0 ? (size_t)e * 2 * I * (H / 32) : 0),
@@ -589,6 +598,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   const size_t wrow_bytes = R == 1 ? (size_t)I / 2 : (size_t)I;
   src.wkb = R == 1 ? 64 : 128;
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
+  src.wend = (uint32_t)((size_t)H * wrow_bytes);
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
   const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
   const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R != 0 ? (size_t)e * H * (I / 32) : 0),

@@ -840,6 +840,7 @@ struct QSrc {
   uint32_t xo[(2 * kQGroups + 3) / 4];
   uint32_t ao, so;
   int akb, skb;                               // bytes per K block of the two scale sources
+  uint32_t wend;                              // bytes of the weight buffer (wr's size)
 };
 
 template <int NC>
@@ -848,11 +849,15 @@ __device__ __forceinline__ int qtoken_block(int w, int j) {
   return b < 2 * NC ? b : 2 * NC - 1;
 }
 
+// Load j of block kb; past the last block (kb >= KB) the weight loads read zeros through a lane
+// offset at the buffer's end (no memory access) and the other loads fetch a copy of block KB - 1.
 template <int NC>
-__device__ __forceinline__ void qissue_load(const StageRef& F, const QSrc& s, int kb, int w, int j) {
+__device__ __forceinline__ void qissue_load(const StageRef& F, const QSrc& s, int kb_, int KB, int w, int j) {
   constexpr int NT = kQTokenLoads<NC>;
+  const int kb = min(kb_, KB - 1);
   if (j < 4) {
-    lds_load16(s.wr, s.wo[j], kb * 64, F.w + (64 * w + 16 * j) * 64);
+    const bool past = kb_ >= KB;
+    lds_load16(s.wr, past ? s.wend : s.wo[j], past ? 0 : kb * 64, F.w + (64 * w + 16 * j) * 64);
   } else if (j < 4 + NT) {
     lds_load16(s.xr, s.xo[j - 4], kb * 128, F.x + qtoken_block<NC>(w, j - 4) * 8 * 128);
   } else if (j == 4 + NT) {
@@ -869,8 +874,9 @@ __device__ __forceinline__ constexpr int qstage_split(int i) {
 }
 
 // K loop: acc[rt][i] += weight tile rt x column group i.  arow0: the lane's LDS row of weight
-// tile 0.  As in the eight-wave kernel, every step issues one stage (past the end a copy of
-// block KB - 1 into a retired slot), so NS - 2 stages of loads stay in flight behind block kb.
+// tile 0.  As in the eight-wave kernel, every step issues one stage (past the end zeros for the
+// weights and a copy of block KB - 1 for the rest, into a retired slot), so NS - 2 stages of
+// loads stay in flight behind block kb.
 template <int NC>
 __device__ __forceinline__ void q_loop(QLds& L, const QSrc& src, int arow0, int KB, v4f acc[4][NC], int w,
                                        int lane) {
@@ -886,17 +892,17 @@ __device__ __forceinline__ void q_loop(QLds& L, const QSrc& src, int arow0, int 
 #pragma unroll
   for (int b = 0; b < NS - 1; ++b) {
 #pragma unroll
-    for (int j = 0; j < kQStageLoads<NC>; ++j) qissue_load<NC>(qstage_ref<NC>(L.ring, b), src, min(b, KB - 1), w, j);
+    for (int j = 0; j < kQStageLoads<NC>; ++j) qissue_load<NC>(qstage_ref<NC>(L.ring, b), src, b, KB, w, j);
   }
   int cur = 0;                               // ring slot of block kb
   for (int kb = 0; kb < KB; ++kb) {
     wait_vmcnt<(NS - 2) * kQStageLoads<NC>>();
     pipeline_barrier();                      // block kb landed for all four waves; kb-1 retired
-    const int ahead = min(kb + NS - 1, KB - 1);
+    const int ahead = kb + NS - 1;
     const StageRef F = qstage_ref<NC>(L.ring, cur == 0 ? NS - 1 : cur - 1);
     auto fetch_part = [&](int i) {
 #pragma unroll
-      for (int j = qstage_split<NC>(i); j < qstage_split<NC>(i + 1); ++j) qissue_load<NC>(F, src, ahead, w, j);
+      for (int j = qstage_split<NC>(i); j < qstage_split<NC>(i + 1); ++j) qissue_load<NC>(F, src, ahead, KB, w, j);
     };
     const StageRef S = qstage_ref<NC>(L.ring, cur);
     cur = cur + 1 == NS ? 0 : cur + 1;
@@ -958,6 +964,7 @@ __device__ __forceinline__ void q_tile(const Args& a, int e, int off, int cnt, i
   src.ar = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
   src.akb = 4 * a.P;
   src.sr = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32), (size_t)H * (I / 32));
+  src.wend = (uint32_t)((size_t)H * (I / 2));
   src.skb = a.wsf_kmajor ? 4 * H : 4;           // K-major weight scales: one K block's rows adjacent
   // output-column permutation of the eight-wave kernel (16 consecutive columns per lane)
   const auto grow = [&](int r) {

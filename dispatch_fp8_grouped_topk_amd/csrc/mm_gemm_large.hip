@@ -283,7 +283,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   const int xrow0 = 16 * wn + lr;
   const int xlo = xrow0 * 128 + 16 * (lg ^ sw7);
   const int xhi = xrow0 * 128 + 16 * ((lg | 4) ^ sw7);
-  int swrow[4];                            // MXFP4: scale word index of each weight tile's row
+  int swrow[4];                            // per-32 recipes: scale word index of each weight tile's row
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
   // Prologue: the issue of steps -(NSW - 1) .. -1.  Every step issues its loads without a

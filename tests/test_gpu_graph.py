@@ -22,7 +22,11 @@ CASES = {
     "mxfp4_shared": synth.Spec(160, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=121,
                                weight_set=121),
     "mxfp8_zipf": synth.Spec(512, 512, 384, 32, 4, recipe=2, routing="zipf", seed=124, weight_set=124),
+    "mxfp4_shared_kmajor_sf": synth.Spec(160, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=125,
+                                         weight_set=125),
 }
+# cases whose weight scales go through the one-time K-major transform first
+KMAJOR = {"mxfp4_shared_kmajor_sf"}
 
 
 def _forward(prob, D, y, ws):
@@ -36,7 +40,11 @@ def test_graph_replay_matches_eager(name):
     print(f"[gpu-graph] {name}: {spec}", flush=True)
     D = to_device(synth.make_problem(spec))
     D_other = to_device(synth.make_problem(replace(spec, seed=spec.seed + 7)))
-    prob = problem_of(spec)
+    prob = problem_of(spec, mm.FLAG_WEIGHT_SF_KMAJOR if name in KMAJOR else 0)
+    if name in KMAJOR:
+        for P in (D, D_other):
+            P["l1_sf"], P["l2_sf"] = mm.mega_moe_transform_weight_scales(prob, P["l1_sf"], P["l2_sf"])
+        torch.cuda.synchronize()
     ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device="cuda")
     y_eager = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device="cuda")
     _forward(prob, D, y_eager, ws)

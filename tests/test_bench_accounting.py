@@ -1,4 +1,4 @@
-"""The benchmark's algorithmic byte and flop counts, against what the inputs and the oracle hold.
+"""The benchmark's algorithmic byte counts, against what the inputs and the oracle hold.
 
 The roofline fraction bench.py reports is achieved / peak with achieved = the algorithmic bytes
 (or flops) of the dominant kernel per launch / its duration, so the counts are checked here

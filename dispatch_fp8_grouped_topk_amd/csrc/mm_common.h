@@ -23,13 +23,16 @@ constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgro
 constexpr int kMaxNGClasses = 8;      // large-M tiles: 1..8 column groups of 16 per wave
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
 
-// Large-M tiling of an expert with c rows: ceil(c / 256) tiles; the ceil(c / 16) row groups of
-// 16 are dealt out evenly (the first G % n tiles take one extra group), so the tiles' group
-// counts differ by at most one.  Tile i starts at row 16 * (i * (G / n) + min(i, G % n)).
+// Large-M tiling of an expert with c rows: ceil(c / 256) tiles over its G = ceil(c / 16) row
+// groups of 16.  The two waves of a SIMD share a tile's groups, so a tile with an odd count
+// computes one padded group; the groups are therefore dealt out in pairs (q = (G / 2) / n pairs
+// each, one more for the first r = (G / 2) % n tiles) and an odd last group goes to tile r, the
+// first tile with q pairs: at most one tile is odd, none has more than 16 groups, and tile 0 is
+// the largest.  Tile i starts at group 2 (i q + min(i, r)) + (G odd and i > r).
 __host__ __device__ inline int large_tiles(int c) { return (c + kLargeRows - 1) / kLargeRows; }
 __host__ __device__ inline int large_tile_start(int c, int i) {
-  const int n = large_tiles(c), g = (c + 15) / 16;
-  return 16 * (i * (g / n) + (i < g % n ? i : g % n));
+  const int n = large_tiles(c), g = (c + 15) / 16, pairs = g / 2, q = pairs / n, r = pairs % n;
+  return 16 * (2 * (i * q + (i < r ? i : r)) + ((g & 1) && i > r ? 1 : 0));
 }
 // Large-M tile-list entry, .x: expert (bits 0-15), rows (bits 16-24), bit 30 set when the tile is
 // its expert's only one (each weight line is then read by exactly one item per slab); .y: the
@@ -42,8 +45,9 @@ __host__ __device__ inline bool tile_single(int x) { return (x & kTileSingle) !=
 // Column groups per wave of the first (largest) tile of an expert with c > 0 rows: the tile's
 // 16-row groups are shared by two waves.
 __host__ __device__ inline int large_first_ng(int c) {
-  const int n = large_tiles(c), g = (c + 15) / 16;
-  return (g / n + (g % n ? 1 : 0) + 1) / 2;
+  const int n = large_tiles(c), g = (c + 15) / 16, pairs = g / 2, q = pairs / n, r = pairs % n;
+  const int g0 = r > 0 ? 2 * q + 2 : 2 * q + (g & 1);
+  return (g0 + 1) / 2;
 }
 
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -9,8 +9,10 @@ quoted on).  Other shapes: --config 0..4.
 
 Prints one JSON line with the layer throughput (algorithmic TFLOP/s, 6*H*I flops per routed
 pair), the weight-stream rate, the dominant kernel's roofline fraction (per-kernel durations
-from HIP events recorded on the library's stream) and, on rank 0 at N=1, the CPU oracle timed
-on a bounded sample of the same workload.
+from HIP events recorded on the library's stream), the median and min of the per-step event
+times and, on rank 0 at N=1, the CPU oracle timed on a bounded sample of the same workload.
+Unless --no-per-config is given, the other benchmark workloads (mid, prefill, MXFP4, and decode
+when another one is selected) are timed the same way after it and reported under per_config.
 """
 import argparse
 import ctypes
@@ -162,6 +164,119 @@ def cpu_baseline(spec, P_dev, n_tokens):
                        f"{dt:.1f} s, numpy float64 block sums")
 
 
+def roofline_of(spec, phase, phase_s, ab, phase_flops, workload_default):
+    """The roofline of one GEMM phase's kernel: whichever of HBM (algorithmic bytes at 8 TB/s)
+    and FP8 MFMA (algorithmic flops at 5 PF) takes longer is its bound; achieved and frac are
+    against that peak for the given duration."""
+    if ab[phase] / (HBM_PEAK_GBPS * 1e9) >= phase_flops[phase] / (FP8_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(ab[phase] / phase_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(phase_flops[phase] / phase_s / 1e12, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    # the committed counters were taken with the default flags and weight-scale layout
+    roof["traffic"] = counted_traffic(phase, spec.name) if workload_default else None
+    return roof
+
+
+def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
+    """Time args.steps forwards of one workload whose inputs P are resident on dev.  Returns the
+    record of the workload: wall-clock ms per step over the whole timed region, the median and
+    min of the per-step HIP-event times, per-phase kernel times and the dominant kernel's
+    roofline."""
+    import numpy as np
+    import torch
+
+    import dispatch_fp8_grouped_topk_amd as mm
+
+    prob = mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, flags)
+    ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device=dev)
+    y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    l1_sf, l2_sf = P["l1_sf"], P["l2_sf"]
+    if kmajor_sf:        # the weight-load-time transform, outside the timed region
+        l1_sf, l2_sf = mm.mega_moe_transform_weight_scales(prob, l1_sf, l2_sf, stream=stream)
+        torch.cuda.synchronize()
+    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], l1_sf, P["l2_w"], l2_sf, y, ws)
+
+    for _ in range(args.warmup):
+        mm.mega_moe_forward(*call, stream=stream)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(mm.NUM_PHASE_EVENTS)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mm.mega_moe_forward_profiled(*call, events=evs[i], stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per_phase = {ph: np.array([hip.elapsed_ms(e[j], e[j + 1]) for e in evs]) for j, ph in enumerate(PHASES)}
+    per_step = np.array([hip.elapsed_ms(e[0], e[-1]) for e in evs])
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+
+    idx_np = P["topk_idx"].cpu().numpy()
+    valid = (idx_np >= 0) & (idx_np < spec.E)
+    pairs = int(valid.sum())
+    touched = int((np.bincount(idx_np[valid], minlength=spec.E) > 0).sum())
+    flops = 6.0 * spec.H * spec.I * pairs
+    phase_flops = {"l1_gemm_swiglu": 4.0 * spec.H * spec.I * pairs, "l2_gemm": 2.0 * spec.H * spec.I * pairs}
+    ab = algorithmic_bytes(spec, touched, pairs)
+    sec = ms_step * 1e-3
+    phase_mean = {k: float(v.mean()) for k, v in per_phase.items()}
+    dom = max(("l1_gemm_swiglu", "l2_gemm"), key=lambda p: phase_mean[p])
+    default_run = args.flags == 0 and not args.rowmajor_sf
+    roof = roofline_of(spec, dom, phase_mean[dom] * 1e-3, ab, phase_flops, default_run)
+    kernels = PHASE_KERNEL_MXFP4 if spec.recipe == 1 and args.flags == 0 else PHASE_KERNEL
+    roof.update(kernel=kernels[dom], phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
+                kernel_ms=round(phase_mean[dom], 4), kernel_ms_median=round(float(np.median(per_phase[dom])), 4),
+                kernel_ms_min=round(float(per_phase[dom].min()), 4))
+    rec = {
+        "workload": spec.name,
+        "ms_per_step": round(ms_step, 4),
+        "gpu_ms_median": round(float(np.median(per_step)), 4),
+        "gpu_ms_min": round(float(per_step.min()), 4),
+        "gpu_ms_mean": round(float(per_step.mean()), 4),
+        "tflops": round(flops / sec / 1e12, 3),
+        "tflops_at_median": round(flops / (np.median(per_step) * 1e-3) / 1e12, 3),
+        "weight_GBps": round(ab["weights"] / sec / 1e9, 1),
+        "tokens_per_s": round(spec.T / sec, 1),
+        "hbm_frac_weights": round(ab["weights"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "mfma_frac": round(flops / sec / 1e12 / FP8_PEAK_TFLOPS, 5),
+        "phase_ms": {k: round(v, 4) for k, v in phase_mean.items()},
+        "phase_ms_median": {k: round(float(np.median(v)), 4) for k, v in per_phase.items()},
+        "roofline": roof,
+        "config": {"T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
+                   "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
+                   "weight_sf": "float-128" if spec.recipe == 0 else ("k-major" if kmajor_sf else "row-major"),
+                   "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
+    }
+    if with_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            mm.mega_moe_forward(*call)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            mm.mega_moe_forward(*call)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        rec["graph_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 4)
+    del ws, y
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +285,9 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the selected workload (by default the mid, prefill and MXFP4 workloads are "
+                         "timed too, after it, and reported under per_config)")
     ap.add_argument("--recipe", type=int, default=None, choices=[0, 1, 2],
                     help="run the workload's shapes and routing with another weight recipe "
                          "(2: E4M3 weights with per-32 UE8M0 scales)")
@@ -191,33 +309,38 @@ def main():
               "HBM and the layer runs without collectives; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import dispatch_fp8_grouped_topk_amd as mm
     import synth
 
-    spec = synth.CONFIGS[args.config]
-    if args.recipe is not None and args.recipe != spec.recipe:
-        wname = ("FP8 float-128", "MXFP4 weights", "E4M3 weights UE8M0 per 32")[args.recipe]
-        spec = dataclasses.replace(spec, recipe=args.recipe, name=f"{spec.name} ({wname})")
+    def spec_of(cfg):
+        spec = synth.CONFIGS[cfg]
+        if args.recipe is not None and args.recipe != spec.recipe:
+            wname = ("FP8 float-128", "MXFP4 weights", "E4M3 weights UE8M0 per 32")[args.recipe]
+            spec = dataclasses.replace(spec, recipe=args.recipe, name=f"{spec.name} ({wname})")
+        return spec
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    P = synth.make_weights(spec, dev)
-    idx, w = synth.make_routing(spec)
-    x, x_sf = synth.make_activations(spec, dev)
-    P.update(x=x, x_sf=x_sf, topk_idx=idx.to(dev), topk_w=w.to(dev))
+    weights = {}
+
+    def inputs(spec):
+        key = (spec.weight_set, spec.H, spec.I, spec.E, spec.recipe)
+        if key not in weights:
+            weights.clear()
+            torch.cuda.empty_cache()
+            weights[key] = synth.make_weights(spec, dev)
+        P = dict(weights[key])
+        idx, w = synth.make_routing(spec)
+        x, x_sf = synth.make_activations(spec, dev)
+        P.update(x=x, x_sf=x_sf, topk_idx=idx.to(dev), topk_w=w.to(dev))
+        return P
+
+    spec = spec_of(args.config)
+    P = inputs(spec)
     kmajor_sf = spec.recipe != 0 and not args.rowmajor_sf
     flags = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if kmajor_sf else 0)
-    prob = mm.Problem.make(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp, flags)
-    ws = torch.empty(mm.mega_moe_workspace_size(prob), dtype=torch.uint8, device=dev)
-    y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    l1_sf, l2_sf = P["l1_sf"], P["l2_sf"]
-    if kmajor_sf:        # the weight-load-time transform, outside the timed region
-        l1_sf, l2_sf = mm.mega_moe_transform_weight_scales(prob, l1_sf, l2_sf, stream=stream)
-        torch.cuda.synchronize()
-    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], l1_sf, P["l2_w"], l2_sf, y, ws)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -228,94 +351,52 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        mm.mega_moe_forward(*call, stream=stream)
-    torch.cuda.synchronize()
-
-    hip = HipEvents()
-    evs = [[hip.create() for _ in range(mm.NUM_PHASE_EVENTS)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        mm.mega_moe_forward_profiled(*call, events=evs[i], stream=stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    phase_ms = {ph: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, ph in enumerate(PHASES)}
-    gpu_ms = float(np.mean([hip.elapsed_ms(e[0], e[-1]) for e in evs]))
-    for e in evs:
-        for h in e:
-            hip.destroy(h)
-
-    idx_np = idx.numpy()
-    valid = (idx_np >= 0) & (idx_np < spec.E)
-    pairs = int(valid.sum())
-    touched = int((np.bincount(idx_np[valid], minlength=spec.E) > 0).sum())
-    flops = 6.0 * spec.H * spec.I * pairs
-    phase_flops = {"l1_gemm_swiglu": 4.0 * spec.H * spec.I * pairs, "l2_gemm": 2.0 * spec.H * spec.I * pairs}
-    ab = algorithmic_bytes(spec, touched, pairs)
-    sec = ms_step * 1e-3
-    # dominant kernel and its roofline: the bound is whichever of HBM (algorithmic bytes) and
-    # FP8 MFMA (algorithmic flops) takes longer at the published peak
-    dom = max(("l1_gemm_swiglu", "l2_gemm"), key=lambda p: phase_ms[p])
-    dom_s = phase_ms[dom] * 1e-3
-    if ab[dom] / (HBM_PEAK_GBPS * 1e9) >= phase_flops[dom] / (FP8_PEAK_TFLOPS * 1e12):
-        roof = {"bound": "hbm", "achieved": round(ab[dom] / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(phase_flops[dom] / dom_s / 1e12, 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    # the committed counters were taken with the default flags and weight-scale layout
-    default_run = args.flags == 0 and not args.rowmajor_sf
-    roof["traffic"] = counted_traffic(dom, spec.name) if default_run else None
-    kernels = PHASE_KERNEL_MXFP4 if spec.recipe == 1 and args.flags == 0 else PHASE_KERNEL
-    roof.update(kernel=kernels[dom], phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
-                kernel_ms=round(phase_ms[dom], 4))
+    rec = measure(spec, args, dev, P, flags, kmajor_sf, with_graph=args.graph)
+    cfg = rec.pop("config")
     out = {
         "metric": "MoE-layer TFLOP/s + weight GB/s vs roofline, H7168 I2048 256e top8",
-        "value": round(flops / sec / 1e12, 3),
+        "value": rec["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {0: "fp8_e4m3", 1: "fp8_e4m3 x fp4_e2m1", 2: "fp8_e4m3 (ue8m0 per 32)"}[spec.recipe],
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, quantised to the layer's formats)",
-        "config": {"workload": spec.name, "T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
-                   "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
-                   "weight_sf": "float-128" if spec.recipe == 0 else ("k-major" if kmajor_sf else "row-major"),
-                   "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
-        "weight_GBps": round(ab["weights"] / sec / 1e9, 1),
-        "tokens_per_s": round(spec.T / sec, 1),
-        "hbm_frac_weights": round(ab["weights"] / sec / 1e9 / HBM_PEAK_GBPS, 4),
-        "mfma_frac": round(flops / sec / 1e12 / FP8_PEAK_TFLOPS, 5),
-        "gpu_ms_per_step": round(gpu_ms, 4),
-        "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
-        "roofline": roof,
+        "config": {"workload": spec.name, **cfg},
+        "ms_per_step_median": rec["gpu_ms_median"],
+        "ms_per_step_min": rec["gpu_ms_min"],
+        "weight_GBps": rec["weight_GBps"],
+        "tokens_per_s": rec["tokens_per_s"],
+        "hbm_frac_weights": rec["hbm_frac_weights"],
+        "mfma_frac": rec["mfma_frac"],
+        "gpu_ms_per_step": rec["gpu_ms_mean"],
+        "phase_ms": rec["phase_ms"],
+        "roofline": rec["roofline"],
     }
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            mm.mega_moe_forward(*call)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            mm.mega_moe_forward(*call)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        out["graph_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / args.steps, 4)
+    if "graph_ms_per_step" in rec:
+        out["graph_ms_per_step"] = rec["graph_ms_per_step"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, P, min(args.cpu_tokens, spec.T))
+    if not args.no_per_config:
+        # the other benchmark workloads, each timed the same way (configs 1 and 3 share weights)
+        per = {}
+        for c in sorted((1, 2, 3, 4), key=lambda c: (c != 3, c)):
+            if c == args.config:
+                continue
+            s = spec_of(c)
+            km = s.recipe != 0 and not args.rowmajor_sf
+            fl = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if km else 0)
+            del P
+            P = inputs(s)
+            r = measure(s, args, dev, P, fl, km)
+            r.pop("config")
+            per[f"config{c}"] = r
+            print(f"[bench] {s.name}: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+        out["per_config"] = per
     print(json.dumps(out), flush=True)
 
 

@@ -32,6 +32,7 @@ FLAG_TILE_LARGE = 2
 FLAG_CLAMP_INPUTS = 4   # with swiglu_clamp > 0: clamp gate and up before SiLU
 FLAG_PRECISE_SILU = 8   # SiLU with expf and IEEE division instead of the hardware exp / rcp
 FLAG_WEIGHT_SF_KMAJOR = 16   # per-32 recipes: weight scales from mega_moe_transform_weight_scales
+FLAG_INTER_SF64 = 32         # FP8 recipe: intermediate float scales per 64 channels (L2 in two halves)
 
 ABI_VERSION = 1
 
@@ -99,6 +100,8 @@ def _load():
     lib.mega_moe_forward_profiled.restype = ctypes.c_int
     lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.mega_moe_diag_mfma_block_sums.restype = ctypes.c_int
+    lib.mega_moe_diag_mfma_block_sums.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     if lib.mega_moe_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH} has ABI {lib.mega_moe_abi_version()}, expected {ABI_VERSION}")
     _lib = lib
@@ -256,6 +259,7 @@ def mega_moe_workspace_views(problem: Problem, workspace) -> dict:
     T, H, I, E, k = (problem.num_tokens, problem.hidden, problem.intermediate,
                      problem.num_experts, problem.topk)
     P = T * k
+    gi = 64 if problem.flags & FLAG_INTER_SF64 else 128     # channels per float intermediate scale
 
     def view(addr, nbytes, dtype, shape):
         off = addr - base
@@ -268,11 +272,35 @@ def mega_moe_workspace_views(problem: Problem, workspace) -> dict:
         pair_pos=view(v.pair_pos, 4 * P, torch.int32, (P,)),
         num_invalid=view(v.num_invalid, 4, torch.int32, (1,)),
         inter_q=view(v.inter_q, P * I, torch.uint8, (P, I)),
-        inter_sf=(view(v.inter_sf, P * (I // 128) * 4, torch.float32, (I // 128, P)).t()
+        inter_sf=(view(v.inter_sf, P * (I // gi) * 4, torch.float32, (I // gi, P)).t()
                   if problem.recipe == RECIPE_FP8_B128 else
                   view(v.inter_sf, P * (I // 32), torch.uint8, (I // 128, P, 4)).permute(1, 0, 2).reshape(P, I // 32)),
         slot=view(v.slot, P * H * 2, torch.int16, (P, H)),
     )
+
+
+def mega_moe_diag_mfma_block_sums(fmt: int, a, b, a_scale=None, b_scale=None, stream=None):
+    """16 x 16 block dot products over one 128-K block with the GEMMs' MFMA instruction.
+    a: uint8 [n, 16, 128] (fmt 1: [n, 16, 64] packed E2M1), b: uint8 [n, 16, 128]; scales uint8
+    [n, 16, 4] for fmt 1 and 2.  Returns float32 [n, 16, 16]."""
+    import torch
+    dev = b.device
+    n = b.shape[0]
+    a_cols = 64 if fmt == 1 else 128
+    _check_tensor("a", a, dev, (torch.uint8,), (n, 16, a_cols))
+    _check_tensor("b", b, dev, (torch.uint8,), (n, 16, 128))
+    if fmt != 0:
+        _check_tensor("a_scale", a_scale, dev, (torch.uint8,), (n, 16, 4))
+        _check_tensor("b_scale", b_scale, dev, (torch.uint8,), (n, 16, 4))
+    out = torch.empty(n, 16, 16, dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _load().mega_moe_diag_mfma_block_sums(int(fmt), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                               _ptr(out), int(n), ctypes.c_void_p(handle))
+    if st:
+        raise MegaMoEError(st, "mega_moe_diag_mfma_block_sums")
+    return out
 
 
 class MegaMoE:

@@ -35,7 +35,10 @@ int check_problem(const mega_moe_problem* p) {
     return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU |
-                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR))
+                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR | MEGA_MOE_FLAG_INTER_SF64))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  // per-64 float intermediate scales exist for the float-scale recipe only
+  if ((p->flags & MEGA_MOE_FLAG_INTER_SF64) && p->recipe != MEGA_MOE_RECIPE_FP8_B128)
     return MEGA_MOE_ERR_INVALID_ARG;
   // the K-major weight-scale layout exists for the per-32 (UE8M0) recipes only
   if ((p->flags & MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR) && p->recipe == MEGA_MOE_RECIPE_FP8_B128)
@@ -69,7 +72,8 @@ Layout make_layout(const mega_moe_problem* p) {
   L.tiles_l = take(tl * 8);
   L.x_sf_pool = take(P * (H / 128) * 4);
   L.inter_q = take(P * I);
-  L.inter_sf = take(p->recipe == MEGA_MOE_RECIPE_FP8_B128 ? P * (I / 128) * 4 : P * (I / 32));
+  const size_t inter_groups = (p->flags & MEGA_MOE_FLAG_INTER_SF64) ? I / 64 : I / 128;
+  L.inter_sf = take(p->recipe == MEGA_MOE_RECIPE_FP8_B128 ? P * inter_groups * 4 : P * (I / 32));
   L.slot = take(P * H * 2);
   L.total = o;
   return L;
@@ -208,13 +212,14 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.clamp_inputs = (p->flags & MEGA_MOE_FLAG_CLAMP_INPUTS) != 0;
   a.precise_silu = (p->flags & MEGA_MOE_FLAG_PRECISE_SILU) != 0;
   a.wsf_kmajor = (p->flags & MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR) != 0;
+  a.inter64 = (p->flags & MEGA_MOE_FLAG_INTER_SF64) != 0;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
   a.large_min_rows = mm::kLargeMinRows;
   a.max_tiles_s = L.max_tiles_s;
   a.max_tiles_l = L.max_tiles_l;
-  // the large-M kernels address token rows with 32-bit byte offsets: larger problems go small
-  if ((uint64_t)a.T * (uint64_t)a.H >= (1ull << 32) || (uint64_t)a.P * (uint64_t)a.I >= (1ull << 32))
-    a.tile_mode = 1;
+  // the large-M kernels address activations, the intermediate and the pool-order scale words
+  // through 32-bit buffer descriptors and offsets: larger problems go to the small-M kernels
+  if (!mm::large_kernels_addressable(a.T, a.H, a.I, a.k)) a.tile_mode = 1;
   const int cus = device_cus();
   if (cus <= 0) return MEGA_MOE_ERR_HIP;
   a.large_grid = cus < 8 ? 8 : cus / 8 * 8;
@@ -296,6 +301,21 @@ MM_EXPORT int mega_moe_transform_weight_scales(const mega_moe_problem* p, const 
                            H / 128, s) != hipSuccess ||
       mm::launch_sf_kmajor(static_cast<const uint32_t*>(l2_sf), static_cast<uint32_t*>(l2_sf_kmajor), E, H,
                            I / 128, s) != hipSuccess)
+    return MEGA_MOE_ERR_HIP;
+  return MEGA_MOE_OK;
+}
+
+MM_EXPORT int mega_moe_diag_mfma_block_sums(int fmt, const void* a, const void* b, const void* a_scale,
+                                            const void* b_scale, float* out, int n_tiles, void* stream) {
+  if (fmt < 0 || fmt > 2 || n_tiles < 0) return MEGA_MOE_ERR_INVALID_ARG;
+  if (n_tiles == 0) return MEGA_MOE_OK;
+  if (!a || !b || !out || (fmt != 0 && (!a_scale || !b_scale))) return MEGA_MOE_ERR_NULL_POINTER;
+  if (misaligned(a) || misaligned(b) || misaligned(out)) return MEGA_MOE_ERR_MISALIGNED;
+  const int st = check_device();
+  if (st) return st;
+  if (mm::launch_diag_mfma(fmt, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b),
+                           static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale), out,
+                           n_tiles, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MEGA_MOE_ERR_HIP;
   return MEGA_MOE_OK;
 }

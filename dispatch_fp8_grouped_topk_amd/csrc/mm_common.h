@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mm_policy.h"
+
 namespace mm {
 
 // ------------------------------------------------------------------------------------------
@@ -13,7 +15,6 @@ constexpr int kMaxExperts = 8192;     // LDS arrays of the scan kernel hold one 
 constexpr int kMaxTopk = 64;
 constexpr int kRouteBlock = 256;      // pairs per dispatch workgroup
 constexpr int kSmallRows = 64;        // pool rows per small-M tile (4 MFMA column groups of 16)
-constexpr int kLargeRows = 256;       // most pool rows per large-M tile
 // Auto mode: experts with at least this many rows use the large-M class.  Measured on MI355X,
 // the persistent large-M kernel (three-deep operand ring for small tiles) is at least as fast
 // as the small-M kernels down to single-row experts, so it takes every expert.
@@ -23,17 +24,6 @@ constexpr int kL2SlabRows = 256;      // output columns (w2 rows) per L2 workgro
 constexpr int kMaxNGClasses = 8;      // large-M tiles: 1..8 column groups of 16 per wave
 constexpr int kMaxKBlocks = 128;      // H/128 and I/128 limit (LDS scale staging)
 
-// Large-M tiling of an expert with c rows: ceil(c / 256) tiles over its G = ceil(c / 16) row
-// groups of 16.  The two waves of a SIMD share a tile's groups, so a tile with an odd count
-// computes one padded group; the groups are therefore dealt out in pairs (q = (G / 2) / n pairs
-// each, one more for the first r = (G / 2) % n tiles) and an odd last group goes to tile r, the
-// first tile with q pairs: at most one tile is odd, none has more than 16 groups, and tile 0 is
-// the largest.  Tile i starts at group 2 (i q + min(i, r)) + (G odd and i > r).
-__host__ __device__ inline int large_tiles(int c) { return (c + kLargeRows - 1) / kLargeRows; }
-__host__ __device__ inline int large_tile_start(int c, int i) {
-  const int n = large_tiles(c), g = (c + 15) / 16, pairs = g / 2, q = pairs / n, r = pairs % n;
-  return 16 * (2 * (i * q + (i < r ? i : r)) + ((g & 1) && i > r ? 1 : 0));
-}
 // Large-M tile-list entry, .x: expert (bits 0-15), rows (bits 16-24), bit 30 set when the tile is
 // its expert's only one (each weight line is then read by exactly one item per slab); .y: the
 // tile's first pool row.
@@ -41,14 +31,6 @@ constexpr int kTileSingle = 1 << 30;
 __host__ __device__ inline int tile_expert(int x) { return x & 0xFFFF; }
 __host__ __device__ inline int tile_rows(int x) { return (x >> 16) & 0x1FF; }
 __host__ __device__ inline bool tile_single(int x) { return (x & kTileSingle) != 0; }
-
-// Column groups per wave of the first (largest) tile of an expert with c > 0 rows: the tile's
-// 16-row groups are shared by two waves.
-__host__ __device__ inline int large_first_ng(int c) {
-  const int n = large_tiles(c), g = (c + 15) / 16, pairs = g / 2, q = pairs / n, r = pairs % n;
-  const int g0 = r > 0 ? 2 * q + 2 : 2 * q + (g & 1);
-  return (g0 + 1) / 2;
-}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -102,6 +84,8 @@ struct Args {
   int quad_grid;        // its workgroups (two per CU, multiple of 8)
   int wsf_kmajor;       // per-32 recipes: weight scales as [E][K/128][rows] words (4 UE8M0 codes
                         // of one 128-K block of one row), else [E][rows][K/32] bytes
+  int inter64;          // FP8 recipe: the intermediate has a float scale per 64 channels, inter_sf
+                        // [I/64][P]; L2 sums each 128-K block as two 64-K halves
 };
 
 // ------------------------------------------------------------------------------------------
@@ -207,6 +191,20 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row_kblock, int l
   return r;
 }
 
+// One 64-K half of an FP8 operand, the other half zeroed: by the layout above, a lane's bytes
+// 0..15 lie in K [0, 64) of the block and its bytes 16..31 in K [64, 128), so an MFMA with
+// half H of one operand sums exactly the products of that half of the block.
+template <int H>
+__device__ __forceinline__ v8i fp8_half(const v8i& b) {
+  v8i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = H == 0 ? b[i] : 0;
+    r[4 + i] = H == 1 ? b[4 + i] : 0;
+  }
+  return r;
+}
+
 __device__ __forceinline__ v8i load_fp4_operand(const uint8_t* row_kblock_packed, int lg) {
   v4i lo = *reinterpret_cast<const v4i*>(row_kblock_packed + 16 * lg);
   v8i r;
@@ -241,4 +239,7 @@ hipError_t launch_l2_large(const Args& a, hipStream_t s);
 hipError_t launch_combine(const Args& a, hipStream_t s);
 // out[e][kb][r] = in[e][r][kb] over E experts of `rows` rows and KB words per row (32-bit words)
 hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s);
+// n_tiles 16 x 16 block dot products with the GEMMs' MFMA (fmt as in mega_moe_diag_mfma_block_sums)
+hipError_t launch_diag_mfma(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                            float* out, int n_tiles, hipStream_t s);
 }  // namespace mm

@@ -168,7 +168,7 @@ struct Src {
   uint32_t co;
   int wkb;                                    // bytes per K block of a weight row
   uint32_t wend;                              // bytes of the weight buffer (wr's size)
-  int ckb;                                    // bytes per K block of this wave's scale source
+  uint32_t ckb;                               // bytes per K block of this wave's scale source
 };
 
 template <int R>
@@ -212,7 +212,7 @@ __device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int 
   } else if (jt < NT) {
     lds_load16(s.xr, s.xo[jt], bt * 128, F.x + token_block<NG>(w, jt) * 8 * 128);
   } else {
-    lds_load4(s.cr, s.co, bt * s.ckb, F.scl + 64 * w);
+    lds_load4(s.cr, s.co, (int)((uint32_t)bt * s.ckb), F.scl + 64 * w);
   }
 }
 
@@ -269,8 +269,10 @@ __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
 
 // The K loop shared by L1 and L2 for a wave with NG column groups: acc[rt][i] (+)= weight tile
 // rt x column group 2i + wn.  arow0: the lane's LDS row of weight tile 0; wsel[rt]: the FP8
-// weight-scale block (L.wsc row) of tile rt.
-template <int R, int NG, bool L1, bool NTW>
+// weight-scale block (L.wsc row) of tile rt.  H64 (FP8 L2 with per-64 intermediate scales): each
+// 128-K block is two MFMAs, one per 64-K half of the token operand (the other half zeroed), each
+// promoted with its own activation scale (stage words [0, 256) and [256, 512)).
+template <int R, int NG, bool L1, bool NTW, bool H64 = false>
 __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const int wsel[4], int KB,
                                        v4f acc[4][NG], int w, int wn, int lane) {
   constexpr int NSW = Ring<R, NG>::kWStages, NST = Ring<R, NG>::kTStages;
@@ -352,7 +354,43 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         sw8[4] = hi[0]; sw8[5] = hi[1]; sw8[6] = hi[2]; sw8[7] = hi[3];
       }
     };
-    if (R == 0) {
+    if (R == 0 && H64) {
+      float cw[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
+      read_token_scales();                 // first-half scales
+      uint32_t sh8[8];                     // second-half scales of column groups 0..NG-1
+      {
+        const v4i lo = *reinterpret_cast<const v4i*>(S.scl + 256 + tsp);
+        sh8[0] = lo[0]; sh8[1] = lo[1]; sh8[2] = lo[2]; sh8[3] = lo[3];
+        if (NG > 4) {
+          const v4i hi = *reinterpret_cast<const v4i*>(S.scl + 256 + tsp + 4);
+          sh8[4] = hi[0]; sh8[5] = hi[1]; sh8[6] = hi[2]; sh8[7] = hi[3];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        v8i Bn;
+        if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
+        const v8i B0 = fp8_half<0>(B), B1 = fp8_half<1>(B);
+        v4f q0[4], q1[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          q0[rt] = mfma_fp8(A[rt], B0);
+          q1[rt] = mfma_fp8(A[rt], B1);
+        }
+        const float s0 = __uint_as_float(sw8[i]), s1 = __uint_as_float(sh8[i]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt][i] += q0[rt] * (s0 * cw[rt]);
+          acc[rt][i] += q1[rt] * (s1 * cw[rt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_part(i);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < NG) B = Bn;
+      }
+    } else if (R == 0) {
       const v8i B1 = NG > 1 ? lds_fp8_operand(xl, xh, 4096) : B;
       v4f p[2][4];
 #pragma unroll
@@ -419,7 +457,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       }
     }
   }
-  if (R == 0) {
+  if (R == 0 && !H64) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += pend[rt] * pend_s[rt];
   }
@@ -435,10 +473,13 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 // the expert, a row's scale word of K block kb sits at grow(r) * wsrow_bytes + kb * wskb (row-major
 // scales: one row's words are consecutive; K-major: one K block's rows are, so a wave's 64 rows
 // are 256 contiguous bytes instead of 64 cache lines).
+// h64 (FP8 recipe, L2 with per-64 intermediate scales, [I/64][P] words): K block kb's two halves
+// are scale rows 2 kb and 2 kb + 1; waves 0-3 fetch the first half's words and waves 4-7, which
+// have no weight scales to fetch in this recipe, the second half's into words [256, 512).
 template <int R, int NG, class F>
 __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, rsrc_t sf_pool,
                                               int P, int off, int cnt, rsrc_t w_sf, F grow,
-                                              uint32_t wsrow_bytes, int wskb, int w, int lane) {
+                                              uint32_t wsrow_bytes, int wskb, int w, int lane, bool h64 = false) {
 #pragma unroll
   for (int j = 0; j < kTokenLoads<NG>; ++j) {
     const int r = 8 * token_block<NG>(w, j) + (lane >> 3);
@@ -446,11 +487,12 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
   }
   const int d = 64 * (w & 3) + lane;
   const bool wscale = R != 0 && w >= 4;
+  const bool half2 = R == 0 && h64;
   s.cr = wscale ? w_sf : sf_pool;
-  s.ckb = wscale ? wskb : 4 * P;
-  if (w < 4) {
+  s.ckb = wscale ? (uint32_t)wskb : 4u * (half2 ? 2u : 1u) * (uint32_t)P;
+  if (w < 4 || half2) {
     const int r = tok_scale_row(d);
-    s.co = 4u * (uint32_t)(off + (r < cnt ? r : cnt - 1));
+    s.co = 4u * (uint32_t)(off + (r < cnt ? r : cnt - 1)) + (w >= 4 ? 4u * (uint32_t)P : 0u);
   } else {
     s.co = R != 0 ? (uint32_t)grow(d) * wsrow_bytes : 0u;   // FP8: one word, read by every lane
   }
@@ -571,7 +613,10 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int col = 16 * (2 * i + wn) + lr;
-      const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+      // per-128 scales: the group is the slab (all four row groups); per-64: row groups 2h, 2h+1
+      const int h = wm >> 1;
+      const float amax = a.inter64 ? fmaxf(red[2 * h][col], red[2 * h + 1][col])
+                                   : fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
       const float sf = amax / 448.0f, m = 448.0f / amax;
       const bool valid = col < cnt;
       uint2 q = make_uint2(0u, 0u);
@@ -581,13 +626,14 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
       }
       if (valid)
         *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
-      if (valid && wm == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)slab * a.P + off + col] = sf;
+      if (valid && lg == 0 && (a.inter64 ? (wm & 1) == 0 : wm == 0))
+        static_cast<float*>(a.inter_sf)[(size_t)(a.inter64 ? 2 * slab + h : slab) * a.P + off + col] = sf;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------ L2
-template <int R, int NG, bool NTW>
+template <int R, int NG, bool NTW, bool H64>
 __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int cnt, int slab, Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -600,7 +646,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
   src.wend = (uint32_t)((size_t)H * wrow_bytes);
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
-  const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
+  const rsrc_t sf_pool = make_rsrc(a.inter_sf, (size_t)KB * (H64 ? 2 : 1) * a.P * 4);
   const rsrc_t w_sf = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (R != 0 ? (size_t)e * H * (I / 32) : 0),
                                 (size_t)H * (I / 32));
   // Tile row 64 wm + 16 rt + m holds output column 64 wm + 16 (m / 4) + 4 rt + m % 4 of the
@@ -614,7 +660,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   };
   weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
   token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : I / 32,
-                       a.wsf_kmajor ? 4 * H : 4, w, lane);
+                       a.wsf_kmajor ? 4 * H : 4, w, lane, H64);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = wm >> 1;
@@ -624,7 +670,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R, NG, false, NTW>(L, src, 64 * wm + lr, wsel, KB, acc, w, wn, lane);
+  k_loop<R, NG, false, NTW, H64>(L, src, 64 * wm + lr, wsel, KB, acc, w, wn, lane);
 
   const int nbase = kWRows * slab + 64 * wm;
   if (nbase >= H) return;                        // wave-uniform: H is a multiple of 128
@@ -670,7 +716,7 @@ __device__ __forceinline__ ItemPos item_pos(int q, int n_slabs, int n_tiles) {
 // Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
 // The item's tile-list entry is in L.td_next (fetched during the previous item); q_next is the
 // workgroup's next item (-1: none), whose entry this item fetches in turn.
-template <int R, bool L1>
+template <int R, bool L1, bool H64>
 __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n_slabs, int n_tiles, Lds& L) {
   const int tid = threadIdx.x;
   const int slab = item_pos(q, n_slabs, n_tiles).slab;
@@ -723,10 +769,10 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   case n:                                                                            \
     if (R != 1 && nt) {                                                              \
       if (L1) l1_large_tile<R, n, R != 1>(a, e, off, cnt, slab, L);                  \
-      else l2_large_tile<R, n, R != 1>(a, e, off, cnt, slab, L);                     \
+      else l2_large_tile<R, n, R != 1, H64>(a, e, off, cnt, slab, L);                \
     } else {                                                                         \
       if (L1) l1_large_tile<R, n, false>(a, e, off, cnt, slab, L);                   \
-      else l2_large_tile<R, n, false>(a, e, off, cnt, slab, L);                      \
+      else l2_large_tile<R, n, false, H64>(a, e, off, cnt, slab, L);                 \
     }                                                                                \
     break;
     MM_CASE(1) MM_CASE(2) MM_CASE(3) MM_CASE(4) MM_CASE(5) MM_CASE(6) MM_CASE(7)
@@ -737,7 +783,9 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
 
 // Persistent item loop over the items numbered as above.  Round r gives XCD x
 // (hardware workgroup id mod 8) the items r*G + x*(G/8) + j for its workgroups j.
-template <int R, bool L1>
+// H64: the FP8 L2 GEMM with per-64 intermediate scales (a kernel of its own, so the default
+// kernels' code and register allocation do not carry its two-MFMA blocks).
+template <int R, bool L1, bool H64 = false>
 __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   __shared__ __attribute__((aligned(1024))) Lds L;
   const int n_slabs = L1 ? a.I / kL1SlabCh : (a.H + kWRows - 1) / kWRows;
@@ -766,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[item_pos(q, n_slabs, n_tiles).tile];
   for (int r = 0; q >= 0; ++r) {
     const int q_next = r + 1 < rounds ? item(r + 1) : -1;
-    run_item<R, L1>(a, q, q_next, n_slabs, n_tiles, L);
+    run_item<R, L1, H64>(a, q, q_next, n_slabs, n_tiles, L);
     q = q_next;
   }
 }
@@ -839,7 +887,7 @@ struct QSrc {
   uint32_t wo[4];
   uint32_t xo[(2 * kQGroups + 3) / 4];
   uint32_t ao, so;
-  int akb, skb;                               // bytes per K block of the two scale sources
+  uint32_t akb, skb;                          // bytes per K block of the two scale sources
   uint32_t wend;                              // bytes of the weight buffer (wr's size)
 };
 
@@ -861,9 +909,9 @@ __device__ __forceinline__ void qissue_load(const StageRef& F, const QSrc& s, in
   } else if (j < 4 + NT) {
     lds_load16(s.xr, s.xo[j - 4], kb * 128, F.x + qtoken_block<NC>(w, j - 4) * 8 * 128);
   } else if (j == 4 + NT) {
-    lds_load4(s.ar, s.ao, kb * s.akb, F.scl + 64 * w);
+    lds_load4(s.ar, s.ao, (int)((uint32_t)kb * s.akb), F.scl + 64 * w);
   } else {
-    lds_load4(s.sr, s.so, kb * s.skb, F.scl + 256 + 64 * w);
+    lds_load4(s.sr, s.so, (int)((uint32_t)kb * s.skb), F.scl + 256 + 64 * w);
   }
 }
 
@@ -962,10 +1010,10 @@ __device__ __forceinline__ void q_tile(const Args& a, int e, int off, int cnt, i
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * (I / 2), (size_t)H * (I / 2));
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
   src.ar = make_rsrc(a.inter_sf, (size_t)KB * a.P * 4);
-  src.akb = 4 * a.P;
+  src.akb = 4u * (uint32_t)a.P;
   src.sr = make_rsrc(static_cast<const uint8_t*>(a.l2_sf) + (size_t)e * H * (I / 32), (size_t)H * (I / 32));
   src.wend = (uint32_t)((size_t)H * (I / 2));
-  src.skb = a.wsf_kmajor ? 4 * H : 4;           // K-major weight scales: one K block's rows adjacent
+  src.skb = a.wsf_kmajor ? 4u * (uint32_t)H : 4u;   // K-major weight scales: one K block's rows adjacent
   // output-column permutation of the eight-wave kernel (16 consecutive columns per lane)
   const auto grow = [&](int r) {
     const int m = r & 15, rt = (r >> 4) & 3;
@@ -1039,7 +1087,9 @@ __global__ __launch_bounds__(kQThreads, 2) void k_quad_l2(Args a) {
 template <bool L1>
 hipError_t launch_large(const Args& a, hipStream_t s) {
   if (a.max_tiles_l == 0 || a.tile_mode == 1) return hipSuccess;
-  if (a.recipe == 0) hipLaunchKernelGGL((k_large<0, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  if (a.recipe == 0 && a.inter64 && !L1)
+    hipLaunchKernelGGL((k_large<0, false, true>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
+  else if (a.recipe == 0) hipLaunchKernelGGL((k_large<0, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
   else if (a.recipe == 1) hipLaunchKernelGGL((k_large<1, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((k_large<2, L1>), dim3(a.large_grid), dim3(kThreads), 0, s, a);
   if constexpr (!L1)

@@ -214,7 +214,10 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const int col = 16 * s + lr;
-      const float amax = fmaxf(fmaxf(s_red[col], s_red[64 + col]), fmaxf(s_red[128 + col], s_red[192 + col]));
+      // per-128 scales: the group is the slab (all four waves' channels); per-64: waves 2h, 2h+1
+      const int h = w >> 1;
+      const float amax = a.inter64 ? fmaxf(s_red[2 * h * 64 + col], s_red[(2 * h + 1) * 64 + col])
+                                   : fmaxf(fmaxf(s_red[col], s_red[64 + col]), fmaxf(s_red[128 + col], s_red[192 + col]));
       const float sf = amax / 448.0f, m = 448.0f / amax;
       const bool valid = col < cnt;
 #pragma unroll
@@ -224,7 +227,8 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
         if (valid)
           *reinterpret_cast<uint32_t*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * w + 16 * i + 4 * lg) = q;
       }
-      if (valid && w == 0 && lg == 0) static_cast<float*>(a.inter_sf)[(size_t)slab * a.P + off + col] = sf;
+      if (valid && lg == 0 && (a.inter64 ? (w & 1) == 0 : w == 0))
+        static_cast<float*>(a.inter_sf)[(size_t)(a.inter64 ? 2 * slab + h : slab) * a.P + off + col] = sf;
     }
   }
 }
@@ -259,12 +263,14 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
   const int off = a.offset[e] + m0;
 
   if (tid < 64) s_src[tid] = a.pool_src[off + (tid < cnt ? tid : cnt - 1)];
+  // float scales per 128 (KS = KB per row) or per 64 (KS = 2 KB: the two halves of each block)
+  const int KS = a.inter64 ? 2 * KB : KB;
   if (R == 0) {
-    float* sfa = reinterpret_cast<float*>(s_scale);           // [64][KB]
+    float* sfa = reinterpret_cast<float*>(s_scale);           // [64][KS]
     const float* isf = static_cast<const float*>(a.inter_sf);
-    for (int i = tid; i < 64 * KB; i += kThreads) {
-      const int row = i / KB;
-      sfa[i] = isf[(size_t)(i % KB) * a.P + off + (row < cnt ? row : cnt - 1)];
+    for (int i = tid; i < 64 * KS; i += kThreads) {
+      const int row = i / KS;
+      sfa[i] = isf[(size_t)(i % KS) * a.P + off + (row < cnt ? row : cnt - 1)];
     }
   } else {
     const int G4 = I / 128;                                    // words of 4 UE8M0 codes per row
@@ -317,11 +323,22 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
       const float sb = sfw[kb];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        const float c = sfa[(16 * s + lr) * KB + kb] * sb;
+        if (a.inter64) {                    // one MFMA per 64-K half, each with its own scale
+          const float c0 = sfa[(16 * s + lr) * KS + 2 * kb] * sb, c1 = sfa[(16 * s + lr) * KS + 2 * kb + 1] * sb;
+          const v8i B0 = fp8_half<0>(B[s]), B1 = fp8_half<1>(B[s]);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const v4f p = mfma_fp8(A[rt], B[s]);
-          acc[rt][s] += p * c;
+          for (int rt = 0; rt < 4; ++rt) {
+            const v4f p0 = mfma_fp8(A[rt], B0), p1 = mfma_fp8(A[rt], B1);
+            acc[rt][s] += p0 * c0;
+            acc[rt][s] += p1 * c1;
+          }
+        } else {
+          const float c = sfa[(16 * s + lr) * KB + kb] * sb;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const v4f p = mfma_fp8(A[rt], B[s]);
+            acc[rt][s] += p * c;
+          }
         }
       }
 #pragma unroll
@@ -379,7 +396,8 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void k_l2_small(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_scale[kLdsScaleBytes];
+  // per-64 intermediate scales: two floats per 128-K block of each of the 64 rows
+  __shared__ __attribute__((aligned(16))) uint8_t s_scale[2 * kLdsScaleBytes];
   __shared__ int s_src[64];
   const int q = xcd_logical_id(blockIdx.x, gridDim.x);
   const int n_slabs = (a.H + kL2SlabRows - 1) / kL2SlabRows;

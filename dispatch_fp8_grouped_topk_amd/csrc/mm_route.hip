@@ -261,8 +261,6 @@ hipError_t launch_route(const Args& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------- combine
-// grid (ceil(H / 2048), min(T, 65535)); each thread owns 8 consecutive columns of a token
-// and strides over tokens.
 // One thread per (token, 8 output columns), grid-stride over all of them.  The slot rows of a
 // token are fetched 8 top-k slots at a time (their pair_pos words first, then every active
 // row's 16 bytes), so each thread keeps several loads in flight; the sum is still taken in

@@ -80,7 +80,7 @@ typedef enum {
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
    2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU,
-   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR; other bits must be 0. */
+   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, bit 5 MEGA_MOE_FLAG_INTER_SF64; other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
@@ -100,6 +100,14 @@ typedef enum {
  * 32-bit words, each the four UE8M0 codes of one row's 128-K block (K = H, rows = 2I for l1_sf;
  * K = I, rows = H for l2_sf).  Same sizes as the row-major layout; the results are identical. */
 #define MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR 16u
+/* flags bit 5 (MEGA_MOE_RECIPE_FP8_B128 only; INVALID_ARG with the per-32 recipes): the SM90
+ * design's per-64 intermediate scales.  The L1 epilogue re-quantises the SwiGLU output with one
+ * float scale amax/448 per 64 channels instead of per 128, and the L2 GEMM sums each 128-K block
+ * of w2 as two 64-K halves, each scaled by its own intermediate scale times the block's weight
+ * scale (design page "MegaMoE SM90 Implementation Design", section 5.4, L2 per-64 dual-half
+ * scale application; section 10.1 step 6, the per-64 scale layout).  The inter_sf view is then
+ * [I/64, T*k] float32. */
+#define MEGA_MOE_FLAG_INTER_SF64 32u
 
 enum {
   MEGA_MOE_OK = 0,
@@ -124,7 +132,12 @@ typedef struct {
   uint32_t flags;        /* MEGA_MOE_FLAG_* */
 } mega_moe_problem;
 
-/* Device pointers into a workspace after a forward call (for inspection and tests). */
+/* Device pointers into a workspace after a forward call (for inspection and tests): the buffer
+   views the pages' buffer query hands back for correctness checks of the dispatch state (research
+   report "MegaMoE on SM100/SM90", section 6.4, the buffer-size query that lays out the workspace,
+   pools and combine buffer and returns tensor views of them; development log of the SM90 port,
+   first entry, the Phase 1 buffer query returning its views).  Every pointer lies inside the
+   caller's workspace; nothing is allocated. */
 typedef struct {
   const int32_t* expert_count;   /* [E]   rows per expert */
   const int32_t* expert_offset;  /* [E+1] exclusive prefix of expert_count */
@@ -133,11 +146,20 @@ typedef struct {
   const int32_t* num_invalid;    /* [1]   ids >= E seen in topk_idx */
   const uint8_t* inter_q;        /* [T*k, I] E4M3 intermediate per pool row */
   const void* inter_sf;          /* K-major: [I/128, T*k] f32 | [I/128, T*k, 4] u8 (the four
-                                    per-32 codes of one 128 block); pool row r, block b at b*T*k+r */
+                                    per-32 codes of one 128 block); pool row r, block b at b*T*k+r;
+                                    with MEGA_MOE_FLAG_INTER_SF64 [I/64, T*k] f32 */
   const uint16_t* slot;          /* [T*k, H] BF16 L2 output per pair (t*k+j order) */
 } mega_moe_views;
 
-/* Bytes of workspace a forward call of this problem needs (alignment 256). */
+/* Bytes of workspace a forward call of this problem needs: the separate sizing query of the
+   pages' interface (research report "MegaMoE on SM100/SM90", section 6.4, key APIs: the buffer-size
+   query; design page "MegaMoE SM90 Implementation Design", section 16.1, the SM90 entry's size
+   query registered beside the forward).  The workspace holds the dispatch counts and offsets,
+   the pool metadata, the GEMM tile lists, the pool-order activation scales, the E4M3 intermediate
+   with its scales and the BF16 slot rows, each region 256-byte aligned.  A forward accepts any
+   workspace of at least this many bytes (a >= check, not ==).
+   Errors: NULL_POINTER (p or bytes_out), INVALID_ARG (a field out of range); *bytes_out is
+   written only on success. */
 int mega_moe_workspace_size(const mega_moe_problem* p, size_t* bytes_out);
 
 /* The layer forward; see the top of this file for the arithmetic and the layouts.
@@ -193,9 +215,29 @@ int mega_moe_forward_stats(const mega_moe_problem* p,
 int mega_moe_transform_weight_scales(const mega_moe_problem* p, const void* l1_sf, const void* l2_sf,
                                      void* l1_sf_kmajor, void* l2_sf_kmajor, void* stream);
 
-/* Fill *out with device pointers into `workspace` for problem p. */
+/* Fill *out with device pointers into `workspace` for problem p (the layout of
+   mega_moe_workspace_size; see mega_moe_views).  The views stay valid while the workspace does and
+   hold the last forward's results until the next call that uses the workspace.
+   Errors: NULL_POINTER (p, workspace or out), INVALID_ARG (a field out of range). */
 int mega_moe_workspace_views(const mega_moe_problem* p, const void* workspace,
                              mega_moe_views* out);
+
+/* Diagnostic: n_tiles independent 16 x 16 block dot products over one 128-long K block, computed
+   with the same matrix-core instruction, operand layout and scale encoding the grouped GEMMs use,
+   so that the error of the hardware block sum against the exact sum of its products can be
+   measured (it bounds how far an intermediate value, and so its E4M3 code, may lie from the
+   exactly summed one; design page "MegaMoE SM90 Implementation Design", section 20.3, tolerance,
+   and the development log entry of 2026-06-18 01:10 on accumulator error and E4M3 code flips).
+     out[t][m][n] = sum_{k<128} A[t][m][k] * B[t][n][k] * 2^(sa[t][m][k/32]-127) * 2^(sb[t][n][k/32]-127)
+   fmt 0: A, B E4M3FN bytes [n_tiles][16][128], unit scales (scale arrays ignored, may be NULL);
+   fmt 1: A E2M1 nibbles [n_tiles][16][64] (low nibble = even k), B E4M3FN [n_tiles][16][128],
+          UE8M0 scales sa, sb [n_tiles][16][4];
+   fmt 2: A, B E4M3FN [n_tiles][16][128] with UE8M0 scales sa, sb [n_tiles][16][4].
+   out: float32 [n_tiles][16][16].  Device pointers, 16-byte aligned (scales: any alignment).
+   Enqueued on `stream` (a hipStream_t, NULL for the default stream).  Errors: INVALID_ARG (fmt or
+   n_tiles), NULL_POINTER, MISALIGNED, UNSUPPORTED_DEVICE, HIP. */
+int mega_moe_diag_mfma_block_sums(int fmt, const void* a, const void* b, const void* a_scale,
+                                  const void* b_scale, float* out, int n_tiles, void* stream);
 
 /* Static text for a status code. */
 const char* mega_moe_strerror(int status);

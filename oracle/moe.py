@@ -68,10 +68,19 @@ class Problem:
     recipe: int = RECIPE_FP8_B128
     swiglu_clamp: float = 0.0
     clamp_inputs: bool = False     # clamp gate and up before SiLU instead of silu(gate) * up
+    inter_sf64: bool = False       # FP8 recipe: intermediate re-quantised with a float scale per 64
 
     @property
     def group(self) -> int:
+        """K block of the input scales (activations and weights)."""
         return 128 if self.recipe == RECIPE_FP8_B128 else 32
+
+    @property
+    def inter_group(self) -> int:
+        """Channels per scale of the re-quantised intermediate: the input block, or 64 for the
+        SM90 design's per-64 float scales (design page section 5.4, the L1 epilogue writing one
+        float scale per 64 output columns, and section 10.1 step 6, the per-64 scale layout)."""
+        return 64 if self.inter_sf64 else self.group
 
 
 # --------------------------------------------------------------------------- dispatch
@@ -128,12 +137,13 @@ def _weight_scales_rows(prob: Problem, sf: np.ndarray, n_rows: int) -> np.ndarra
     return C.ue8m0_decode(sf)                                            # [rows, K/32]
 
 
-def block_scaled_gemm(prob: Problem, a_vals, a_scale, b_vals, b_scale) -> np.ndarray:
+def block_scaled_gemm(prob: Problem, a_vals, a_scale, b_vals, b_scale, group: int = 0) -> np.ndarray:
     """sum_kb a_scale[m,kb] * b_scale[n,kb] * sum_{k in kb} a[m,k] * b[n,k]  (float64).
 
-    a_vals [M, K], a_scale [M, K/G], b_vals [N, K], b_scale [N, K/G]; G = K block.
+    a_vals [M, K], a_scale [M, K/G], b_vals [N, K], b_scale [N, K/G]; G = K block (group, or the
+    recipe's input block when 0).
     """
-    G = prob.group
+    G = group or prob.group
     M, K = a_vals.shape
     N = b_vals.shape[0]
     out = np.zeros((M, N), dtype=np.float64)
@@ -169,7 +179,7 @@ def requant(prob: Problem, v: np.ndarray):
     Returns (codes u8 [n, I], scales [n, I/G] (float32, or UE8M0 u8), dequantised float64).
     """
     n, I = v.shape
-    G = prob.group
+    G = prob.inter_group
     v32 = v.astype(np.float32).reshape(n, I // G, G)
     amax = np.max(np.abs(v32), axis=2)                                     # float32, exact
     if prob.recipe == RECIPE_FP8_B128:
@@ -193,13 +203,19 @@ def requant(prob: Problem, v: np.ndarray):
 
 # --------------------------------------------------------------------------- forward
 def expert_rows(prob: Problem, e: int, t_rows: np.ndarray, w_rows: np.ndarray,
-                x, x_sf, l1_w, l1_sf, l2_w, l2_sf) -> dict:
-    """Everything one expert does to a set of its pool rows (token ids t_rows)."""
+                x, x_sf, l1_w, l1_sf, l2_w, l2_sf, magnitudes: bool = False) -> dict:
+    """Everything one expert does to a set of its pool rows (token ids t_rows).
+
+    magnitudes: also return l1_abs, the same block-scaled sum over the magnitudes of every
+    product, sum_kb |sa| |sb| sum_k |a| |b| (what bounds the rounding error of any summation
+    order of the L1 products; the tests derive their intermediate-code tolerance from it)."""
     a = _act_values(prob, x[t_rows])
     sa = _act_scales(prob, x_sf[t_rows])
     w1 = _weight_values(prob, l1_w[e])
     s1 = _weight_scales_rows(prob, l1_sf[e], 2 * prob.I)
     acc = block_scaled_gemm(prob, a, sa, w1, s1)                           # [n, 2I]
+    l1_abs = (block_scaled_gemm(prob, np.abs(a), np.abs(sa), np.abs(w1), np.abs(s1))
+              if magnitudes else None)
     v = swiglu_weighted(prob, acc, w_rows)
     q, qsf, vd = requant(prob, v)
     w2 = _weight_values(prob, l2_w[e])
@@ -208,18 +224,24 @@ def expert_rows(prob: Problem, e: int, t_rows: np.ndarray, w_rows: np.ndarray,
         sq = qsf.astype(np.float64)
     else:
         sq = np.ldexp(1.0, qsf.astype(np.int64) - 127)
-    o = block_scaled_gemm(prob, C.e4m3_decode(q), sq, w2, s2)              # [n, H]
+    # per-64 intermediate scales: each 128-K block of w2 is summed as two 64-K halves, each with
+    # its own activation scale and the block's weight scale (design page section 5.4)
+    Gi = prob.inter_group
+    s2 = np.repeat(s2, prob.group // Gi, axis=1) if Gi < prob.group else s2
+    o = block_scaled_gemm(prob, C.e4m3_decode(q), sq, w2, s2, group=Gi)    # [n, H]
     slot = C.bf16_bits_rne(o.astype(np.float32))
-    return dict(l1_acc=acc, v=v, inter_q=q, inter_sf=qsf, o=o, slot=slot)
+    return dict(l1_acc=acc, l1_abs=l1_abs, v=v, inter_q=q, inter_sf=qsf, o=o, slot=slot)
 
 
 def forward(prob: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf,
-            tokens=None) -> dict:
+            tokens=None, magnitudes: bool = False) -> dict:
     """The layer forward.  ``tokens`` (optional) restricts the work to those tokens.
 
     Returns y (BF16 bits, [len(tokens) or T, H]), the dispatch result, and per
     pool row (only rows of the selected tokens) the intermediate codes/scales
-    and the BF16 slot rows.
+    and the BF16 slot rows.  With ``magnitudes``, also per pool row the L1
+    result (l1_acc), its magnitude sum (l1_abs, see expert_rows), the
+    pre-quantisation value v (float64) and the row's top-k weight.
     """
     T, k = prob.T, prob.k
     idx = np.asarray(topk_idx)
@@ -230,6 +252,7 @@ def forward(prob: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf,
     want[sel] = True
     slot = {}            # pair -> BF16 bits [H]
     inter_q, inter_sf = {}, {}
+    extra = dict(l1_acc={}, l1_abs={}, v={}, w={}) if magnitudes else {}
     for e in range(prob.E):
         rows = d["src"][d["offset"][e]:d["offset"][e + 1]]
         rows = rows[want[rows // k]]
@@ -237,12 +260,17 @@ def forward(prob: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf,
             continue
         t_rows = rows // k
         w_rows = w.reshape(-1)[rows]
-        r = expert_rows(prob, e, t_rows, w_rows, x, x_sf, l1_w, l1_sf, l2_w, l2_sf)
+        r = expert_rows(prob, e, t_rows, w_rows, x, x_sf, l1_w, l1_sf, l2_w, l2_sf, magnitudes)
         for i, pair in enumerate(rows):
             p = int(d["pos"][pair])
             slot[int(pair)] = r["slot"][i]
             inter_q[p] = r["inter_q"][i]
             inter_sf[p] = r["inter_sf"][i]
+            if magnitudes:
+                extra["l1_acc"][p] = r["l1_acc"][i]
+                extra["l1_abs"][p] = r["l1_abs"][i]
+                extra["v"][p] = r["v"][i]
+                extra["w"][p] = float(w_rows[i])
     y = np.zeros((sel.size, prob.H), dtype=np.uint16)
     for i, t in enumerate(sel):
         acc = np.zeros(prob.H, dtype=np.float32)
@@ -251,7 +279,7 @@ def forward(prob: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf,
             if pair in slot:
                 acc = (acc + C.bf16_bits_to_f32(slot[pair])).astype(np.float32)
         y[i] = C.bf16_bits_rne(acc)
-    return dict(y=y, tokens=sel, dispatch=d, slot=slot, inter_q=inter_q, inter_sf=inter_sf)
+    return dict(y=y, tokens=sel, dispatch=d, slot=slot, inter_q=inter_q, inter_sf=inter_sf, **extra)
 
 
 def flops(prob: Problem, n_pairs: int) -> float:

@@ -49,6 +49,7 @@ class Spec:
     routing: str = "uniform"   # uniform | biased | zipf | uniform_shared
     swiglu_clamp: float = 0.0
     clamp_inputs: bool = False     # the clamp applies to gate and up before SiLU
+    inter_sf64: bool = False       # FP8 recipe: intermediate scales per 64 channels instead of 128
     seed: int = 1000
     weight_set: int = 0
     w_std: float = 0.02
@@ -57,6 +58,11 @@ class Spec:
     @property
     def group(self) -> int:
         return 128 if self.recipe == RECIPE_FP8 else 32
+
+    @property
+    def inter_group(self) -> int:
+        """Channels per scale of the re-quantised intermediate."""
+        return 64 if self.inter_sf64 else self.group
 
     @property
     def pairs(self) -> int:

@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) against the CPU oracle, on an MI355X.
 
 Small problems are compared in full (every output element, every dispatch field, every
-intermediate code); the benchmark-size workloads are compared on sampled tokens, with the
-dispatch metadata still checked in full.
+intermediate code).  At the benchmark sizes the decode and mid workloads are compared in full;
+the prefill and MXFP4 workloads on a stratified sample of tokens (every tile of the hottest
+experts, every column-group class), with the dispatch metadata always checked in full.
 """
 import sys
 from dataclasses import replace
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from harness import (assert_dispatch_exact, assert_intermediate_close, assert_y_close, problem_of, run_gpu,
                      run_oracle, to_device)
@@ -66,9 +68,15 @@ SMALL = {
                                           clamp_inputs=True, seed=132, weight_set=132),
     "mxfp8_clamp": synth.Spec(64, 512, 256, 8, 4, recipe=2, routing="biased", swiglu_clamp=0.05, seed=133,
                               weight_set=133),
-    # more than 16384 pairs: dispatch runs 1024 pairs per workgroup; skewed so that experts
-    # fill every large-M column-group class
+    # 16800 pairs over 66 dispatch workgroups of 256 pairs; skewed so that experts fill every
+    # large-M column-group class
     "wide_dispatch": synth.Spec(2100, 512, 256, 64, 8, routing="zipf", seed=115, weight_set=115),
+    # per-64 float intermediate scales (flag MEGA_MOE_FLAG_INTER_SF64): ragged sizes, every
+    # column-group class under Zipf routing, the output clamp, two 64-groups per L1 slab
+    "sf64": synth.Spec(37, 640, 384, 12, 3, inter_sf64=True, seed=150, weight_set=150),
+    "sf64_zipf": synth.Spec(512, 512, 384, 32, 4, routing="zipf", inter_sf64=True, seed=151, weight_set=151),
+    "sf64_clamp": synth.Spec(64, 512, 256, 8, 4, routing="biased", swiglu_clamp=0.05, inter_sf64=True, seed=152,
+                             weight_set=152),
 }
 
 
@@ -89,7 +97,8 @@ def test_precise_silu(name, flags):
 
 @pytest.mark.parametrize("flags", [1, 2], ids=["small_only", "large_only"])
 @pytest.mark.parametrize("name", ["ragged", "multi_tile", "zipf", "mxfp4", "mxfp4_multi_tile", "clamp_inputs",
-                                  "mxfp4_clamp_inputs", "mxfp8", "mxfp8_multi_tile", "mxfp8_zipf_clamp_inputs"])
+                                  "mxfp4_clamp_inputs", "mxfp8", "mxfp8_multi_tile", "mxfp8_zipf_clamp_inputs",
+                                  "sf64", "sf64_zipf", "sf64_clamp"])
 def test_forced_tile_class(name, flags):
     spec = SMALL[name]
     _full_check(spec, synth.make_problem(spec), flags)
@@ -252,12 +261,14 @@ def test_one_hot_weights_equal_selected_slot():
 _DEV_CACHE = {}
 
 
-def _device_problem(cfg, recipe=None):
+def _device_problem(cfg, recipe=None, sf64=False):
     """Benchmark-size inputs generated on the GPU (weights shared between configs 1 and 3);
-    ``recipe`` replaces the workload's weight recipe."""
+    ``recipe`` replaces the workload's weight recipe, ``sf64`` selects per-64 intermediate scales."""
     spec = synth.CONFIGS[cfg]
     if recipe is not None:
         spec = replace(spec, recipe=recipe, name=f"{spec.name} recipe {recipe}")
+    if sf64:
+        spec = replace(spec, inter_sf64=True, name=f"{spec.name} per-64 intermediate scales")
     key = (spec.weight_set, spec.H, spec.I, spec.E, spec.recipe)
     if key not in _DEV_CACHE:
         _DEV_CACHE.clear()
@@ -270,54 +281,111 @@ def _device_problem(cfg, recipe=None):
     return spec, P
 
 
-def _sample_tokens(spec, idx, n=3):
-    counts = np.bincount(idx[idx >= 0].reshape(-1), minlength=spec.E)
-    hot = int(np.argmax(counts))
-    last_hot = int(np.nonzero((idx == hot).any(axis=1))[0][-1])     # deepest row of the hottest pool
-    toks = [0, spec.T - 1, last_hot][:n]
-    return sorted(set(toks))
+def _tile_starts(c):
+    """Row ranges of the large-M tiles of an expert with c rows: ceil(c / 256) tiles over its
+    16-row groups, dealt out in pairs, an odd last group going to the first tile with the smaller
+    pair count (the split the route kernel writes into the tile list)."""
+    n = (c + 255) // 256
+    g = (c + 15) // 16
+    pairs = g // 2
+    q, r = divmod(pairs, n)
+    st = [16 * (2 * (i * q + min(i, r)) + (1 if (g & 1) and i > r else 0)) for i in range(n)]
+    return list(zip(st, st[1:] + [c]))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_benchmark_config_sampled_parity(cfg):
-    spec, P = _device_problem(cfg)
-    _say(f"config {cfg}: {spec.name}")
-    y, views, _ = run_gpu(spec, P)
+def _stratified_tokens(spec, idx):
+    """Tokens whose pool rows cover: the first and last row of every large-M tile of the 8 hottest
+    experts (every tile of a multi-tile expert there, the odd-group tile included), the first and
+    last row of every tile of two experts of each column-group class 1..8 present (so every
+    instantiation of the GEMM kernels, and the four-wave MXFP4 L2 kernel's tile sizes, are
+    checked), the shared expert's tiles where there is one, and the first and last token."""
+    d = oracle.route(idx, spec.E)
+    count, offset, src = d["count"], d["offset"], d["src"]
+    pick = set()
+
+    def take_expert(e):
+        for m0, m1 in _tile_starts(int(count[e])):
+            for m in (m0, m1 - 1):
+                pick.add(int(src[offset[e] + m]) // spec.k)
+
+    order = np.argsort(-count, kind="stable")
+    for e in order[:8]:
+        if count[e] > 0:
+            take_expert(int(e))
+    by_class = {}
+    for e in range(spec.E):
+        c = int(count[e])
+        if c == 0:
+            continue
+        m0, m1 = _tile_starts(c)[0]
+        ng = ((m1 - m0 + 15) // 16 + 1) // 2
+        by_class.setdefault(ng, []).append(e)
+    for ng, es in sorted(by_class.items()):
+        for e in es[:2]:
+            take_expert(e)
+    if spec.routing == "uniform_shared":
+        take_expert(spec.E - 1)
+    pick |= {0, spec.T - 1}
+    classes = sorted(by_class)
+    return sorted(pick), classes
+
+
+def _parity_at_size(cfg, recipe=None, flags=0, full=False, sf64=False):
+    spec, P = _device_problem(cfg, recipe=recipe, sf64=sf64)
+    _say(f"config {cfg} recipe {spec.recipe} flags {flags}: {spec.name}")
+    y, views, _ = run_gpu(spec, P, flags)
     idx = P["topk_idx"].cpu().numpy()
-    assert_dispatch_exact(spec, idx, views)
-    toks = _sample_tokens(spec, idx)
-    ref = run_oracle(spec, P, tokens=toks)
-    assert_intermediate_close(spec, views, ref)
-    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
-    _say(f"config {cfg}: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
+    d = assert_dispatch_exact(spec, idx, views)
+    if full:
+        toks, classes = list(range(spec.T)), None
+    else:
+        toks, classes = _stratified_tokens(spec, idx)
+    ref = run_oracle(spec, P, tokens=None if full else toks)
+    frac = assert_intermediate_close(spec, views, ref)
+    yg = y.cpu().numpy() if full else y.cpu().numpy()[toks]
+    rel, mean_rel = assert_y_close(yg, ref["y"], spec.name)
+    pairs = len(ref["inter_q"])
+    _say(f"config {cfg}: {len(toks)} of {spec.T} tokens, {pairs} of {int(d['offset'][-1])} pool rows compared"
+         + (f" (column-group classes {classes})" if classes else "")
+         + f"; codes differing {frac:.3e}; y max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
 
 
-@pytest.mark.parametrize("cfg", [1, 3])
-def test_mxfp8_benchmark_size_sampled_parity(cfg):
-    """The decode and prefill shapes and routing with E4M3 weights and per-32 UE8M0 scales."""
-    spec, P = _device_problem(cfg, recipe=2)
-    _say(f"config {cfg} recipe 2: {spec.name}")
-    y, views, _ = run_gpu(spec, P)
-    idx = P["topk_idx"].cpu().numpy()
-    assert_dispatch_exact(spec, idx, views)
-    toks = _sample_tokens(spec, idx)
-    ref = run_oracle(spec, P, tokens=toks)
-    assert_intermediate_close(spec, views, ref)
-    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
-    _say(f"config {cfg} recipe 2: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_benchmark_config_full_parity(cfg):
+    """Decode and mid workloads at their full sizes: every token, every pool row."""
+    _parity_at_size(cfg, full=True)
 
 
-@pytest.mark.parametrize("cfg,recipe", [(4, None), (3, 2)], ids=["mxfp4_c4", "mxfp8_prefill"])
-def test_weight_sf_kmajor_benchmark_size_sampled_parity(cfg, recipe):
-    """The benchmark shapes of the per-32 recipes with K-major weight scales."""
+def test_mxfp8_decode_full_parity():
+    """The decode workload with E4M3 weights and per-32 UE8M0 scales, every token."""
     import dispatch_fp8_grouped_topk_amd as mm
-    spec, P = _device_problem(cfg, recipe=recipe)
-    _say(f"config {cfg} K-major scales: {spec.name}")
-    y, views, _ = run_gpu(spec, P, mm.FLAG_WEIGHT_SF_KMAJOR)
-    idx = P["topk_idx"].cpu().numpy()
-    assert_dispatch_exact(spec, idx, views)
-    toks = _sample_tokens(spec, idx)
-    ref = run_oracle(spec, P, tokens=toks)
-    assert_intermediate_close(spec, views, ref)
-    rel, mean_rel = assert_y_close(y.cpu().numpy()[toks], ref["y"], spec.name)
-    _say(f"config {cfg} K-major: tokens {toks} max-rel {rel:.3e} mean-rel {mean_rel:.3e}")
+    _parity_at_size(1, recipe=2, flags=mm.FLAG_WEIGHT_SF_KMAJOR, full=True)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_benchmark_config_stratified_parity(cfg):
+    """Prefill and MXFP4 workloads at their full sizes on a stratified sample of tokens (every
+    tile of the hottest experts, every column-group class), dispatch in full."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    _parity_at_size(cfg, flags=mm.FLAG_WEIGHT_SF_KMAJOR if cfg == 4 else 0)
+
+
+def test_mxfp4_rowmajor_sf_stratified_parity():
+    """The MXFP4 workload with the weight scales in their row-major input layout."""
+    _parity_at_size(4)
+
+
+def test_mxfp8_prefill_stratified_parity():
+    """The prefill shape and routing with E4M3 weights and per-32 UE8M0 scales."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    _parity_at_size(3, recipe=2, flags=mm.FLAG_WEIGHT_SF_KMAJOR)
+
+
+def test_sf64_decode_full_parity():
+    """The decode workload with per-64 float intermediate scales, every token."""
+    _parity_at_size(1, full=True, sf64=True)
+
+
+def test_sf64_prefill_stratified_parity():
+    """The prefill workload with per-64 float intermediate scales, stratified tokens."""
+    _parity_at_size(3, sf64=True)

@@ -11,6 +11,7 @@
 """
 import math
 import os
+from dataclasses import replace
 from fractions import Fraction
 
 import numpy as np
@@ -29,7 +30,7 @@ def _np(P):
 
 def _prob(spec):
     return oracle.Problem(spec.T, spec.H, spec.I, spec.E, spec.k, spec.recipe, spec.swiglu_clamp,
-                          spec.clamp_inputs)
+                          spec.clamp_inputs, spec.inter_sf64)
 
 
 # ----------------------------------------------------------------------------- brute force
@@ -116,14 +117,15 @@ def brute_force(spec, P):
                 if c > 0 and not spec.clamp_inputs:      # clamp on silu(g) * u
                     sv = min(max(sv, -c), c)
                 v32.append(np.float32(sv * float(np.float32(tw[t, j]))))
-            # re-quantisation, group by group
+            # re-quantisation, group by group (Gq channels: the input block, or 64)
+            Gq = 64 if spec.inter_sf64 else G
             deq = []
-            for gi in range(I // G):
-                grp = v32[gi * G:(gi + 1) * G]
+            for gi in range(I // Gq):
+                grp = v32[gi * Gq:(gi + 1) * Gq]
                 amax = max(abs(v) for v in grp)
                 if spec.recipe == 0:
                     sf = np.float32(amax) / np.float32(448.0)
-                    codes = [0] * G if sf == 0 else \
+                    codes = [0] * Gq if sf == 0 else \
                         [_nearest_fp8(min(max(float(np.float32(v) / sf), -448.0), 448.0)) for v in grp]
                     gscale = Fraction(float(sf))
                 else:
@@ -131,17 +133,17 @@ def brute_force(spec, P):
                     c = 0
                     while c < 254 and Fraction(2) ** (c - 127) < Fraction(float(r)):
                         c += 1
-                    codes = [0] * G if amax == 0 else \
+                    codes = [0] * Gq if amax == 0 else \
                         [_nearest_fp8(min(max(float(v) * 2.0 ** (127 - c), -448.0), 448.0)) for v in grp]
                     gscale = Fraction(2) ** (c - 127)
                 deq.append((codes, gscale))
-            # L2
+            # L2: each Gq-channel group with its own scale and the weight scale of its K block
             for n in range(H):
                 wv = _row_vals_w(spec, P["l2_w"][e][n])
                 s = Fraction(0)
                 for gi, (codes, gscale) in enumerate(deq):
-                    blk = sum(Fraction(_FP8[codes[i]]) * Fraction(wv[gi * G + i]) for i in range(G))
-                    s += blk * gscale * _scale_w(spec, P["l2_sf"][e], n, gi)
+                    blk = sum(Fraction(_FP8[codes[i]]) * Fraction(wv[gi * Gq + i]) for i in range(Gq))
+                    s += blk * gscale * _scale_w(spec, P["l2_sf"][e], n, gi * Gq // G)
                 o32 = np.float32(float(s))
                 slot = torch.tensor([float(o32)], dtype=torch.float32).to(torch.bfloat16).float().item()
                 tot[n] = np.float32(tot[n] + np.float32(slot))
@@ -160,6 +162,10 @@ BRUTE_SPECS = {
     "mxfp8": synth.Spec(3, 256, 128, 3, 2, recipe=2, seed=18, weight_set=18),
     "mxfp8_shared_clamp": synth.Spec(2, 128, 64, 3, 2, recipe=2, routing="uniform_shared", seed=19,
                                      weight_set=19, swiglu_clamp=0.01),
+    # per-64 float intermediate scales (design page section 5.4): I = 256 gives two 128-K blocks,
+    # four 64-channel groups per row
+    "fp8_sf64": synth.Spec(3, 256, 256, 3, 2, inter_sf64=True, seed=30, weight_set=30),
+    "fp8_sf64_clamp": synth.Spec(3, 256, 128, 3, 2, inter_sf64=True, swiglu_clamp=0.01, seed=31, weight_set=31),
 }
 
 
@@ -254,14 +260,17 @@ def test_input_clamp_above_every_accumulator_changes_nothing(recipe):
 
 
 # ----------------------------------------------------------------------------- re-quantisation
-@pytest.mark.parametrize("recipe", [0, 1, 2])
-def test_requant_invariants(recipe):
+@pytest.mark.parametrize("recipe,sf64", [(0, False), (1, False), (2, False), (0, True)],
+                         ids=["fp8", "mxfp4", "mxfp8", "fp8_sf64"])
+def test_requant_invariants(recipe, sf64):
     rng = np.random.default_rng(4)
-    prob = oracle.Problem(1, 128, 256, 1, 1, recipe=recipe)
+    prob = oracle.Problem(1, 128, 256, 1, 1, recipe=recipe, inter_sf64=sf64)
     v = rng.standard_normal((64, 256)) * 10.0 ** rng.uniform(-4, 3, (64, 1))
     v[3] = 0.0
+    v[5, 64:128] = 0.0                           # one zero 64-group inside a nonzero 128-group
     q, sf, vd = oracle.requant(prob, v)
-    G = prob.group
+    G = prob.inter_group
+    assert sf.shape == (64, 256 // G)
     tab = oracle.e4m3_decode_table()
     qv = tab[q].reshape(64, 256 // G, G)
     v32 = v.astype(np.float32).astype(np.float64).reshape(64, 256 // G, G)
@@ -312,6 +321,30 @@ def test_one_hot_weights_select_one_expert(recipe):
         assert np.array_equal(r["y"][t], r["slot"][t * spec.k + 1])
         for j in (0, 2):
             assert not np.any(oracle.bf16_bits_to_f32(r["slot"][t * spec.k + j]))
+
+
+def test_sf64_reduces_to_sf128_when_second_halves_vanish():
+    """Per-64 intermediate scales equal the per-128 result bit for bit when the second 64
+    channels of every 128-channel group are zero: the first half's per-64 scale is then the
+    group's per-128 scale, the second half is all zero codes with scale 0, and the two-half L2 sum
+    reduces to the one-block sum.  With the halves present the two recipes differ."""
+    spec = synth.Spec(6, 256, 256, 3, 2, seed=32, weight_set=32)
+    P = _np(synth.make_problem(spec))
+    base = oracle.forward(_prob(spec), **P)
+    half = replace(spec, inter_sf64=True)
+    assert not np.array_equal(oracle.forward(_prob(half), **P)["y"], base["y"])
+    I = spec.I
+    for g in range(I // 128):            # up rows of channels 64..127 of each group: zero codes
+        P["l1_w"][:, I + 128 * g + 64:I + 128 * (g + 1), :] = 0
+    base = oracle.forward(_prob(spec), **P)
+    r64 = oracle.forward(_prob(half), **P)
+    assert np.array_equal(r64["y"], base["y"])
+    for p, sf in r64["inter_sf"].items():
+        assert np.array_equal(sf[1::2], np.zeros(I // 128, dtype=np.float32))
+        assert np.array_equal(sf[0::2], base["inter_sf"][p])
+        # equal values (a vanished half is +0 under its zero scale, -0 or +0 under the shared one)
+        tab = oracle.e4m3_decode_table()
+        assert np.array_equal(tab[r64["inter_q"][p]], tab[base["inter_q"][p]])
 
 
 def test_k1_output_is_the_slot():

@@ -100,6 +100,8 @@ def _load():
     lib.mega_moe_forward_profiled.restype = ctypes.c_int
     lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.mega_moe_forward_noalloc.restype = ctypes.c_int
+    lib.mega_moe_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mega_moe_diag_mfma_block_sums.restype = ctypes.c_int
     lib.mega_moe_diag_mfma_block_sums.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     if lib.mega_moe_abi_version() != ABI_VERSION:
@@ -202,6 +204,35 @@ def mega_moe_forward(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l
     added (mega_moe_forward_stats)."""
     _forward(problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace, stream, None,
              recv_stats)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+ERR_SCRATCH_TOO_SMALL = -7
+
+
+def mega_moe_forward_noalloc(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,
+                             stream=None) -> None:
+    """mega_moe_forward without a workspace: the library's static per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) serves instead, so nothing is allocated.  Calls that overlap on one GPU
+    race on that scratch; larger problems raise MegaMoEError with ERR_SCRATCH_TOO_SMALL."""
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("mega_moe_forward_noalloc needs device tensors")
+    shapes = expected_shapes(problem)
+    tensors = dict(x=x, x_sf=x_sf, topk_idx=topk_idx, topk_w=topk_w, l1_w=l1_w, l1_sf=l1_sf,
+                   l2_w=l2_w, l2_sf=l2_sf, y=y)
+    for name, t in tensors.items():
+        dts, shp = shapes[name]
+        _check_tensor(name, t, dev, dts, shp)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _load().mega_moe_forward_noalloc(ctypes.byref(problem), _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                                          _ptr(topk_w), _ptr(l1_w), _ptr(l1_sf), _ptr(l2_w), _ptr(l2_sf),
+                                          _ptr(y), ctypes.c_void_p(handle))
+    if st:
+        raise MegaMoEError(st, "mega_moe_forward_noalloc")
 
 
 def mega_moe_forward_profiled(problem: Problem, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y,

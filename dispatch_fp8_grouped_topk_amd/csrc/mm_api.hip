@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "mega_moe.h"
 #include "mm_common.h"
@@ -125,6 +126,8 @@ MM_EXPORT const char* mega_moe_strerror(int status) {
     case MEGA_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mega_moe_workspace_size()";
     case MEGA_MOE_ERR_UNSUPPORTED_DEVICE: return "the current device is not gfx950 (MI355X)";
     case MEGA_MOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case MEGA_MOE_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace than the static scratch of mega_moe_forward_noalloc (32 MiB)";
     default: return "unknown status";
   }
 }
@@ -247,6 +250,48 @@ MM_EXPORT int mega_moe_forward(const mega_moe_problem* p, const void* x, const v
                                void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, workspace,
                       workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+// ----------------------------------------------------------------------------- no-alloc forward
+// The workspace of mega_moe_forward_noalloc: a static device array, one copy per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever passed to the kernels.
+static __device__ __align__(256) uint8_t scratch[MEGA_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device (null: not looked up)
+
+// The current device's scratch address, or null when the lookup fails.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+MM_EXPORT int mega_moe_forward_noalloc(const mega_moe_problem* p, const void* x, const void* x_sf,
+                                       const int32_t* topk_idx, const float* topk_w, const void* l1_w,
+                                       const void* l1_sf, const void* l2_w, const void* l2_sf, void* y,
+                                       void* stream) {
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->num_tokens == 0) return MEGA_MOE_OK;
+  if (make_layout(p).total > (size_t)MEGA_MOE_NOALLOC_SCRATCH_BYTES) return MEGA_MOE_ERR_SCRATCH_TOO_SMALL;
+  st = check_device();
+  if (st) return st;
+  void* ws = device_scratch();
+  if (!ws) return MEGA_MOE_ERR_HIP;
+  return forward_impl(p, x, x_sf, topk_idx, topk_w, l1_w, l1_sf, l2_w, l2_sf, y, ws,
+                      (size_t)MEGA_MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0, nullptr);
 }
 
 MM_EXPORT int mega_moe_forward_stats(const mega_moe_problem* p, const void* x, const void* x_sf,

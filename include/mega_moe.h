@@ -116,7 +116,9 @@ enum {
   MEGA_MOE_ERR_MISALIGNED = -3,         /* a pointer is not 16-byte aligned */
   MEGA_MOE_ERR_WORKSPACE_TOO_SMALL = -4,/* workspace_bytes < mega_moe_workspace_size() */
   MEGA_MOE_ERR_UNSUPPORTED_DEVICE = -5, /* the current device is not gfx950 */
-  MEGA_MOE_ERR_HIP = -6                 /* a HIP runtime call or launch failed */
+  MEGA_MOE_ERR_HIP = -6,                /* a HIP runtime call or launch failed */
+  MEGA_MOE_ERR_SCRATCH_TOO_SMALL = -7   /* mega_moe_forward_noalloc: the problem needs more workspace
+                                           than the library's static scratch holds */
 };
 
 typedef struct {
@@ -186,6 +188,25 @@ int mega_moe_forward_profiled(const mega_moe_problem* p,
                               const void* l2_w, const void* l2_sf,
                               void* y, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* events, int num_events);
+
+/* mega_moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+   tight serving loops, harnesses that forbid allocation): no workspace argument; the call uses
+   the library's own static device scratch of MEGA_MOE_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU,
+   which each GPU the library runs on holds until the process ends.  Problems whose
+   mega_moe_workspace_size exceeds it are rejected with MEGA_MOE_ERR_SCRATCH_TOO_SMALL before
+   anything is enqueued (the decode shape T = 128, H = 7168, I = 2048, E = 256, k = 8 needs
+   16.3 MiB; about 250 tokens fit at that shape).  The call allocates, frees and synchronises
+   nothing.  Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+   different streams, or from several threads) race and must be ordered by the caller; the scratch
+   keeps the last call's contents, and each call re-initialises everything it reads.  Same
+   arguments, results and errors as mega_moe_forward otherwise (bit-identical y). */
+#define MEGA_MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mega_moe_forward_noalloc(const mega_moe_problem* p,
+                             const void* x, const void* x_sf,
+                             const int32_t* topk_idx, const float* topk_w,
+                             const void* l1_w, const void* l1_sf,
+                             const void* l2_w, const void* l2_sf,
+                             void* y, void* stream);
 
 /* mega_moe_forward that also adds each expert's received row count (its pool size: pairs
    routed to it, masked and invalid slots excluded) of this call to the caller's device array

@@ -35,8 +35,22 @@ def test_library_exports_every_declared_function():
 def test_abi_version_and_strerror():
     assert mm.mega_moe_abi_version() == mm.ABI_VERSION
     assert mm.mega_moe_strerror(0) == "ok"
-    for st in range(-6, 0):
+    for st in range(-7, 0):
         assert mm.mega_moe_strerror(st) != "unknown status"
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch_before_touching_a_device():
+    """mega_moe_forward_noalloc checks the problem's workspace size against its static scratch
+    first: a problem that does not fit is refused (no pointer or device is looked at)."""
+    lib = mm.library()
+    big = _p(T=4096)                       # 0.5 GiB of workspace at the decode shape
+    assert mm.mega_moe_workspace_size(big) > mm.NOALLOC_SCRATCH_BYTES
+    st = lib.mega_moe_forward_noalloc(ctypes.byref(big), *([None] * 9), None)
+    assert st == mm.ERR_SCRATCH_TOO_SMALL
+    assert "static scratch" in mm.mega_moe_strerror(st)
+    bad = _p(H=100)
+    assert lib.mega_moe_forward_noalloc(ctypes.byref(bad), *([None] * 9), None) == -1
+    assert lib.mega_moe_forward_noalloc(ctypes.byref(_p(T=0)), *([None] * 9), None) == 0
 
 
 def _p(**kw):

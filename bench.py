@@ -228,12 +228,23 @@ def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
     ab = algorithmic_bytes(spec, touched, pairs)
     sec = ms_step * 1e-3
     phase_mean = {k: float(v.mean()) for k, v in per_phase.items()}
-    dom = max(("l1_gemm_swiglu", "l2_gemm"), key=lambda p: phase_mean[p])
     default_run = args.flags == 0 and not args.rowmajor_sf
-    roof = roofline_of(spec, dom, phase_mean[dom] * 1e-3, ab, phase_flops, default_run)
-    kernels = PHASE_KERNEL_MXFP4 if spec.recipe == 1 and args.flags == 0 else PHASE_KERNEL
-    roof.update(kernel=kernels[dom], phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
-                kernel_ms=round(phase_mean[dom], 4), kernel_ms_median=round(float(np.median(per_phase[dom])), 4),
+    if flags & mm.FLAG_FUSED:
+        # one kernel runs the whole layer: its roofline is the layer's (weights and the layer's
+        # inputs and output moved once, 6 H I flops per pair)
+        ab["fused"] = ab["weights"] + ab["io"]
+        phase_flops["fused"] = flops
+        per_phase["fused"] = per_step
+        dom = "fused"
+        roof = roofline_of(spec, dom, float(per_step.mean()) * 1e-3, ab, phase_flops, default_run)
+        kernel = "k_fused"
+    else:
+        dom = max(("l1_gemm_swiglu", "l2_gemm"), key=lambda p: phase_mean[p])
+        roof = roofline_of(spec, dom, phase_mean[dom] * 1e-3, ab, phase_flops, default_run)
+        kernel = (PHASE_KERNEL_MXFP4 if spec.recipe == 1 and args.flags == 0 else PHASE_KERNEL)[dom]
+    roof.update(kernel=kernel, phase=dom, algorithmic_bytes=ab[dom], algorithmic_flops=phase_flops[dom],
+                kernel_ms=round(float(per_phase[dom].mean()), 4),
+                kernel_ms_median=round(float(np.median(per_phase[dom])), 4),
                 kernel_ms_min=round(float(per_phase[dom].min()), 4))
     rec = {
         "workload": spec.name,
@@ -253,7 +264,8 @@ def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
         "config": {"T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
                    "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
                    "weight_sf": "float-128" if spec.recipe == 0 else ("k-major" if kmajor_sf else "row-major"),
-                   "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched},
+                   "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched,
+                   "fused": bool(flags & mm.FLAG_FUSED)},
     }
     if with_graph:
         g = torch.cuda.CUDAGraph()
@@ -295,6 +307,8 @@ def main():
                     help="per-32 recipes: pass the weight scales in their row-major input layout instead of "
                          "the K-major copy the one-time weight-scale transform writes at load time")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
+    ap.add_argument("--fused", action="store_true",
+                    help="the fused forward (MEGA_MOE_FLAG_FUSED): the whole layer in one cooperative launch")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one forward into a HIP graph and time --steps replays "
                          "(reported as graph_ms_per_step; value stays the eager rate)")
@@ -340,6 +354,8 @@ def main():
     spec = spec_of(args.config)
     P = inputs(spec)
     kmajor_sf = spec.recipe != 0 and not args.rowmajor_sf
+    if args.fused:
+        args.flags |= mm.FLAG_FUSED
     flags = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if kmajor_sf else 0)
 
     if args.copy_calibration_mib > 0:

@@ -33,6 +33,7 @@ FLAG_CLAMP_INPUTS = 4   # with swiglu_clamp > 0: clamp gate and up before SiLU
 FLAG_PRECISE_SILU = 8   # SiLU with expf and IEEE division instead of the hardware exp / rcp
 FLAG_WEIGHT_SF_KMAJOR = 16   # per-32 recipes: weight scales from mega_moe_transform_weight_scales
 FLAG_INTER_SF64 = 32         # FP8 recipe: intermediate float scales per 64 channels (L2 in two halves)
+FLAG_FUSED = 64              # the whole forward in one persistent cooperative launch
 
 ABI_VERSION = 1
 

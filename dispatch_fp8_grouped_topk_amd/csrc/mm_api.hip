@@ -18,7 +18,7 @@ namespace {
 
 struct Layout {
   size_t hdr, count, offset, blk, blk_inv, pair_pos, pool_src, w_pool, tiles_s, tiles_l, x_sf_pool,
-      inter_q, inter_sf, slot, total;
+      inter_q, inter_sf, slot, tile_done, total;
   int P, NB, max_tiles_s, max_tiles_l;
 };
 
@@ -36,7 +36,10 @@ int check_problem(const mega_moe_problem* p) {
     return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU |
-                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR | MEGA_MOE_FLAG_INTER_SF64))
+                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR | MEGA_MOE_FLAG_INTER_SF64 | MEGA_MOE_FLAG_FUSED))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  // the fused forward runs the large-M GEMMs only
+  if ((p->flags & MEGA_MOE_FLAG_FUSED) && (p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_SMALL)
     return MEGA_MOE_ERR_INVALID_ARG;
   // per-64 float intermediate scales exist for the float-scale recipe only
   if ((p->flags & MEGA_MOE_FLAG_INTER_SF64) && p->recipe != MEGA_MOE_RECIPE_FP8_B128)
@@ -76,6 +79,7 @@ Layout make_layout(const mega_moe_problem* p) {
   const size_t inter_groups = (p->flags & MEGA_MOE_FLAG_INTER_SF64) ? I / 64 : I / 128;
   L.inter_sf = take(p->recipe == MEGA_MOE_RECIPE_FP8_B128 ? P * inter_groups * 4 : P * (I / 32));
   L.slot = take(P * H * 2);
+  L.tile_done = take((tl + 1) * 4);
   L.total = o;
   return L;
 }
@@ -203,6 +207,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.inter_q = w + L.inter_q;
   a.inter_sf = w + L.inter_sf;
   a.slot = reinterpret_cast<uint16_t*>(w + L.slot);
+  a.tile_done = reinterpret_cast<int32_t*>(w + L.tile_done);
   a.T = (int)p->num_tokens;
   a.H = p->hidden;
   a.I = p->intermediate;
@@ -226,7 +231,10 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   const int cus = device_cus();
   if (cus <= 0) return MEGA_MOE_ERR_HIP;
   a.large_grid = cus < 8 ? 8 : cus / 8 * 8;
-  a.quad = a.recipe == MEGA_MOE_RECIPE_MXFP4W_B32 && a.tile_mode == 0;
+  const bool fused = (p->flags & MEGA_MOE_FLAG_FUSED) != 0;
+  // the fused forward needs every expert in the large-M class, which needs 32-bit offsets
+  if (fused && a.tile_mode == 1) return MEGA_MOE_ERR_INVALID_ARG;
+  a.quad = a.recipe == MEGA_MOE_RECIPE_MXFP4W_B32 && a.tile_mode == 0 && !fused;
   a.quad_grid = 2 * a.large_grid;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -234,6 +242,12 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
     return i >= num_events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
   };
   if (!mark(0)) return MEGA_MOE_ERR_HIP;
+  if (fused) {   // one launch: every phase event after it
+    if (mm::launch_fused(a, s) != hipSuccess) return MEGA_MOE_ERR_HIP;
+    for (int i = 1; i < MEGA_MOE_NUM_PHASE_EVENTS; ++i)
+      if (!mark(i)) return MEGA_MOE_ERR_HIP;
+    return MEGA_MOE_OK;
+  }
   if (mm::launch_route(a, s) != hipSuccess || !mark(1)) return MEGA_MOE_ERR_HIP;
   if (mm::launch_l1_small(a, s) != hipSuccess || mm::launch_l1_large(a, s) != hipSuccess || !mark(2))
     return MEGA_MOE_ERR_HIP;

@@ -40,7 +40,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // kHdrTilesQuad: the first large-M tile (in list order) whose expert's first tile has at most
 // kQuadMaxNG column groups per wave; with the MXFP4 recipe, the L2 GEMM of the tiles from there
 // on runs in the four-wave kernel, two workgroups per CU.
-enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrTilesQuad = 3, kHdrWords = 64 };
+// kHdrFusedFault: set by the fused forward when one of its bounded waits ran out (its results are
+// then invalid).
+enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrTilesQuad = 3, kHdrFusedFault = 4, kHdrWords = 64 };
 constexpr int kQuadMaxNG = 5;
 
 struct Args {
@@ -70,6 +72,8 @@ struct Args {
   uint8_t* inter_q;     // [P, I]
   void* inter_sf;       // [I/128][P] words: f32 | 4 x UE8M0 (K-major, like x_sf_pool)
   uint16_t* slot;       // [P, H] bf16, row = pair
+  int32_t* tile_done;   // fused forward: [max_tiles_l] L1 slabs stored per large-M tile, then the
+                        // number of L1 items stored
   // sizes
   int T, H, I, E, k, P, NB;
   int recipe;
@@ -237,6 +241,8 @@ hipError_t launch_l2_small(const Args& a, hipStream_t s);
 hipError_t launch_l1_large(const Args& a, hipStream_t s);
 hipError_t launch_l2_large(const Args& a, hipStream_t s);
 hipError_t launch_combine(const Args& a, hipStream_t s);
+// the whole forward in one cooperative launch (large-M tiles only)
+hipError_t launch_fused(const Args& a, hipStream_t s);
 // out[e][kb][r] = in[e][r][kb] over E experts of `rows` rows and KB words per row (32-bit words)
 hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s);
 // n_tiles 16 x 16 block dot products with the GEMMs' MFMA (fmt as in mega_moe_diag_mfma_block_sums)

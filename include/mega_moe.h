@@ -80,7 +80,8 @@ typedef enum {
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
    2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU,
-   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, bit 5 MEGA_MOE_FLAG_INTER_SF64; other bits must be 0. */
+   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, bit 5 MEGA_MOE_FLAG_INTER_SF64, bit 6 MEGA_MOE_FLAG_FUSED;
+   other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
@@ -108,6 +109,16 @@ typedef enum {
  * scale application; section 10.1 step 6, the per-64 scale layout).  The inter_sf view is then
  * [I/64, T*k] float32. */
 #define MEGA_MOE_FLAG_INTER_SF64 32u
+/* flags bit 6: the fused forward, the whole layer (dispatch, L1 GEMM + SwiGLU, L2 GEMM, combine)
+ * in one persistent cooperative launch, one workgroup per compute unit (design page "MegaMoE SM90
+ * Implementation Design", section 3.3, the fused kernel pipeline; section 14.3, cross-phase
+ * synchronisation: the L2 GEMM of a pool tile starts as soon as every L1 slab of that tile is
+ * stored, while other L1 work still runs).  Same results bit for bit as the split forward.  Every
+ * expert runs in the large-M class: INVALID_ARG with MEGA_MOE_FLAG_TILE_SMALL or for a problem too
+ * large for the large-M kernels' 32-bit offsets.  Fused forwards on one GPU must not overlap
+ * (each needs every compute unit; cooperative launches are not run side by side).  The events of
+ * mega_moe_forward_profiled are all recorded after the one launch except events[0]. */
+#define MEGA_MOE_FLAG_FUSED 64u
 
 enum {
   MEGA_MOE_OK = 0,

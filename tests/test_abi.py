@@ -76,7 +76,9 @@ def test_workspace_size_grows_with_tokens_and_covers_buffers():
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
                                 dict(k=65), dict(recipe=3), dict(recipe=-1), dict(clamp=-1.0), dict(clamp=float("nan")),
-                                dict(flags=64), dict(flags=3), dict(flags=15), dict(flags=16), dict(T=-1), dict(H=32768),
+                                dict(flags=128), dict(flags=3), dict(flags=15), dict(flags=16), dict(T=-1), dict(H=32768),
+                                # the fused forward runs the large-M tiles only
+                                dict(flags=64 | 1),
                                 # per-64 intermediate scales: the float-scale recipe only
                                 dict(flags=32, recipe=1), dict(flags=32, recipe=2)])
 def test_invalid_problem_rejected(kw):

@@ -35,6 +35,8 @@ PHASES = ("dispatch", "l1_gemm_swiglu", "l2_gemm", "combine")
 PHASE_KERNEL = {"l1_gemm_swiglu": "k_large<L1>", "l2_gemm": "k_large<L2>"}
 PHASE_KERNEL_MXFP4 = {"l1_gemm_swiglu": "k_large<L1>", "l2_gemm": "k_large<L2> + k_quad_l2"}
 KERNEL_SOURCES = ("dispatch_fp8_grouped_topk_amd/csrc/mm_gemm_large.hip",
+                  "dispatch_fp8_grouped_topk_amd/csrc/mm_large_dev.h",
+                  "dispatch_fp8_grouped_topk_amd/csrc/mm_policy.h",
                   "dispatch_fp8_grouped_topk_amd/csrc/mm_common.h")
 TRAFFIC_FILE = os.path.join("profiles", "hbm_traffic.json")
 

@@ -182,6 +182,12 @@ def roofline_of(spec, phase, phase_s, ab, phase_flops, workload_default):
     return roof
 
 
+def paired_flag(spec, args):
+    """MXFP4 weights in the row-pair layout unless --rowmajor-w."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    return mm.FLAG_WEIGHT_E2M1_PAIRED if spec.recipe == 1 and not args.rowmajor_w else 0
+
+
 def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
     """Time args.steps forwards of one workload whose inputs P are resident on dev.  Returns the
     record of the workload: wall-clock ms per step over the whole timed region, the median and
@@ -197,10 +203,14 @@ def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
     y = torch.empty(spec.T, spec.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     l1_sf, l2_sf = P["l1_sf"], P["l2_sf"]
-    if kmajor_sf:        # the weight-load-time transform, outside the timed region
+    if kmajor_sf:        # the weight-load-time transforms, outside the timed region
         l1_sf, l2_sf = mm.mega_moe_transform_weight_scales(prob, l1_sf, l2_sf, stream=stream)
         torch.cuda.synchronize()
-    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], P["l1_w"], l1_sf, P["l2_w"], l2_sf, y, ws)
+    l1_w, l2_w = P["l1_w"], P["l2_w"]
+    if flags & mm.FLAG_WEIGHT_E2M1_PAIRED:
+        l1_w, l2_w = mm.mega_moe_transform_weights(prob, l1_w, l2_w, stream=stream)
+        torch.cuda.synchronize()
+    call = (prob, P["x"], P["x_sf"], P["topk_idx"], P["topk_w"], l1_w, l1_sf, l2_w, l2_sf, y, ws)
 
     for _ in range(args.warmup):
         mm.mega_moe_forward(*call, stream=stream)
@@ -230,7 +240,7 @@ def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
     ab = algorithmic_bytes(spec, touched, pairs)
     sec = ms_step * 1e-3
     phase_mean = {k: float(v.mean()) for k, v in per_phase.items()}
-    default_run = args.flags == 0 and not args.rowmajor_sf
+    default_run = args.flags == 0 and not args.rowmajor_sf and not args.rowmajor_w
     if flags & mm.FLAG_FUSED:
         # one kernel runs the whole layer: its roofline is the layer's (weights and the layer's
         # inputs and output moved once, 6 H I flops per pair)
@@ -266,6 +276,7 @@ def measure(spec, args, dev, P, flags, kmajor_sf, with_graph=False):
         "config": {"T": spec.T, "H": spec.H, "I": spec.I, "E": spec.E, "topk": spec.k,
                    "recipe": ("fp8_b128", "mxfp4w_b32", "mxfp8_b32")[spec.recipe], "routing": spec.routing,
                    "weight_sf": "float-128" if spec.recipe == 0 else ("k-major" if kmajor_sf else "row-major"),
+                   "weights": "row-pairs" if flags & mm.FLAG_WEIGHT_E2M1_PAIRED else "row-major",
                    "swiglu_clamp": spec.swiglu_clamp, "routed_pairs": pairs, "touched_experts": touched,
                    "fused": bool(flags & mm.FLAG_FUSED)},
     }
@@ -308,6 +319,9 @@ def main():
     ap.add_argument("--rowmajor-sf", action="store_true",
                     help="per-32 recipes: pass the weight scales in their row-major input layout instead of "
                          "the K-major copy the one-time weight-scale transform writes at load time")
+    ap.add_argument("--rowmajor-w", action="store_true",
+                    help="MXFP4: E2M1 weights in their row-major input layout (default: the row-pair "
+                         "layout of mega_moe_transform_weights, applied once before timing)")
     ap.add_argument("--flags", type=int, default=0, help="mega_moe_problem.flags (tile class)")
     ap.add_argument("--fused", action="store_true",
                     help="the fused forward (MEGA_MOE_FLAG_FUSED): the whole layer in one cooperative launch")
@@ -358,7 +372,7 @@ def main():
     kmajor_sf = spec.recipe != 0 and not args.rowmajor_sf
     if args.fused:
         args.flags |= mm.FLAG_FUSED
-    flags = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if kmajor_sf else 0)
+    flags = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if kmajor_sf else 0) | paired_flag(spec, args)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -407,7 +421,7 @@ def main():
                 continue
             s = spec_of(c)
             km = s.recipe != 0 and not args.rowmajor_sf
-            fl = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if km else 0)
+            fl = args.flags | (mm.FLAG_WEIGHT_SF_KMAJOR if km else 0) | paired_flag(s, args)
             del P
             P = inputs(s)
             r = measure(s, args, dev, P, fl, km)

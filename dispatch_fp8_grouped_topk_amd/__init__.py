@@ -34,6 +34,7 @@ FLAG_PRECISE_SILU = 8   # SiLU with expf and IEEE division instead of the hardwa
 FLAG_WEIGHT_SF_KMAJOR = 16   # per-32 recipes: weight scales from mega_moe_transform_weight_scales
 FLAG_INTER_SF64 = 32         # FP8 recipe: intermediate float scales per 64 channels (L2 in two halves)
 FLAG_FUSED = 64              # the whole forward in one persistent cooperative launch
+FLAG_WEIGHT_E2M1_PAIRED = 128  # MXFP4: E2M1 weights in the row-pair layout of mega_moe_transform_weights
 
 ABI_VERSION = 1
 
@@ -98,6 +99,8 @@ def _load():
     lib.mega_moe_forward_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.mega_moe_transform_weight_scales.restype = ctypes.c_int
     lib.mega_moe_transform_weight_scales.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.mega_moe_transform_weights.restype = ctypes.c_int
+    lib.mega_moe_transform_weights.argtypes = [P, vp, vp, vp, vp, vp]
     lib.mega_moe_forward_profiled.restype = ctypes.c_int
     lib.mega_moe_forward_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
@@ -195,6 +198,31 @@ def mega_moe_transform_weight_scales(problem: Problem, l1_sf, l2_sf, stream=None
                                                   _ptr(out2), ctypes.c_void_p(handle))
     if st:
         raise MegaMoEError(st, "mega_moe_transform_weight_scales")
+    return out1, out2
+
+
+def mega_moe_transform_weights(problem: Problem, l1_w, l2_w, stream=None):
+    """The MXFP4 recipe's one-time weight transform: returns new tensors of the same shapes
+    (l1 [E, 2I, H/2], l2 [E, H, I/2] uint8) holding the E2M1 weights in the row-pair layout, for
+    forward calls whose problem has FLAG_WEIGHT_E2M1_PAIRED set."""
+    import torch
+    dev = l1_w.device
+    if dev.type != "cuda":
+        raise ValueError("mega_moe_transform_weights needs device tensors")
+    rowmajor = Problem.make(problem.num_tokens, problem.hidden, problem.intermediate, problem.num_experts,
+                            problem.topk, problem.recipe, problem.swiglu_clamp,
+                            problem.flags & ~FLAG_WEIGHT_E2M1_PAIRED)
+    shapes = expected_shapes(rowmajor)
+    for name, t in (("l1_w", l1_w), ("l2_w", l2_w)):
+        _check_tensor(name, t, dev, *shapes[name])
+    out1, out2 = torch.empty_like(l1_w), torch.empty_like(l2_w)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _load().mega_moe_transform_weights(ctypes.byref(rowmajor), _ptr(l1_w), _ptr(l2_w), _ptr(out1),
+                                            _ptr(out2), ctypes.c_void_p(handle))
+    if st:
+        raise MegaMoEError(st, "mega_moe_transform_weights")
     return out1, out2
 
 

@@ -36,7 +36,11 @@ int check_problem(const mega_moe_problem* p) {
     return MEGA_MOE_ERR_INVALID_ARG;
   if (std::isnan(p->swiglu_clamp) || p->swiglu_clamp < 0.f) return MEGA_MOE_ERR_INVALID_ARG;
   if (p->flags & ~(MEGA_MOE_FLAG_TILE_MASK | MEGA_MOE_FLAG_CLAMP_INPUTS | MEGA_MOE_FLAG_PRECISE_SILU |
-                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR | MEGA_MOE_FLAG_INTER_SF64 | MEGA_MOE_FLAG_FUSED))
+                   MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR | MEGA_MOE_FLAG_INTER_SF64 | MEGA_MOE_FLAG_FUSED |
+                   MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  // the row-pair weight layout exists for the E2M1 weights only
+  if ((p->flags & MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED) && p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32)
     return MEGA_MOE_ERR_INVALID_ARG;
   // the fused forward runs the large-M GEMMs only
   if ((p->flags & MEGA_MOE_FLAG_FUSED) && (p->flags & MEGA_MOE_FLAG_TILE_MASK) == MEGA_MOE_FLAG_TILE_SMALL)
@@ -220,6 +224,7 @@ int forward_impl(const mega_moe_problem* p, const void* x, const void* x_sf,
   a.clamp_inputs = (p->flags & MEGA_MOE_FLAG_CLAMP_INPUTS) != 0;
   a.precise_silu = (p->flags & MEGA_MOE_FLAG_PRECISE_SILU) != 0;
   a.wsf_kmajor = (p->flags & MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR) != 0;
+  a.w_paired = (p->flags & MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED) != 0;
   a.inter64 = (p->flags & MEGA_MOE_FLAG_INTER_SF64) != 0;
   a.tile_mode = (int)(p->flags & MEGA_MOE_FLAG_TILE_MASK);
   a.large_min_rows = mm::kLargeMinRows;
@@ -360,6 +365,37 @@ MM_EXPORT int mega_moe_transform_weight_scales(const mega_moe_problem* p, const 
                            H / 128, s) != hipSuccess ||
       mm::launch_sf_kmajor(static_cast<const uint32_t*>(l2_sf), static_cast<uint32_t*>(l2_sf_kmajor), E, H,
                            I / 128, s) != hipSuccess)
+    return MEGA_MOE_ERR_HIP;
+  return MEGA_MOE_OK;
+}
+
+MM_EXPORT int mega_moe_transform_weights(const mega_moe_problem* p, const void* l1_w, const void* l2_w,
+                                         void* l1_w_paired, void* l2_w_paired, void* stream) {
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->recipe != MEGA_MOE_RECIPE_MXFP4W_B32) return MEGA_MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {l1_w, l2_w, l1_w_paired, l2_w_paired};
+  for (const void* q : ptrs)
+    if (!q) return MEGA_MOE_ERR_NULL_POINTER;
+  for (const void* q : ptrs)
+    if (misaligned(q)) return MEGA_MOE_ERR_MISALIGNED;
+  const int H = p->hidden, I = p->intermediate, E = p->num_experts;
+  const auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+  };
+  const size_t n1 = (size_t)E * 2 * I * (H / 2), n2 = (size_t)E * H * (I / 2);
+  if (overlap(l1_w_paired, n1, l1_w, n1) || overlap(l1_w_paired, n1, l2_w, n2) ||
+      overlap(l2_w_paired, n2, l1_w, n1) || overlap(l2_w_paired, n2, l2_w, n2) ||
+      overlap(l1_w_paired, n1, l2_w_paired, n2))
+    return MEGA_MOE_ERR_INVALID_ARG;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mm::launch_e2m1_pairs(static_cast<const uint8_t*>(l1_w), static_cast<uint8_t*>(l1_w_paired),
+                            (size_t)E * I, H / 128, s) != hipSuccess ||
+      mm::launch_e2m1_pairs(static_cast<const uint8_t*>(l2_w), static_cast<uint8_t*>(l2_w_paired),
+                            (size_t)E * H / 2, I / 128, s) != hipSuccess)
     return MEGA_MOE_ERR_HIP;
   return MEGA_MOE_OK;
 }

@@ -42,8 +42,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // on runs in the four-wave kernel, two workgroups per CU.
 // kHdrFusedFault: set by the fused forward when one of its bounded waits ran out (its results are
 // then invalid).
-enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrTilesQuad = 3, kHdrFusedFault = 4, kHdrWords = 64 };
+enum { kHdrInvalid = 0, kHdrTilesSmall = 1, kHdrTilesLarge = 2, kHdrTilesQuad = 3, kHdrFusedFault = 4, kHdrTilesWide = 5,
+       kHdrWords = 64 };
 constexpr int kQuadMaxNG = 5;
+// kHdrTilesWide: the first large-M tile whose expert's first tile has at most kWideMaxNG column
+// groups per wave; with the MXFP4 recipe the L1 GEMM runs the tiles from there as wide items.
+constexpr int kWideMaxNG = 5;
 
 struct Args {
   // inputs
@@ -86,6 +90,7 @@ struct Args {
   int large_grid;       // workgroups of the persistent large-M kernels (multiple of 8)
   int quad;             // 1: MXFP4 L2 tiles of at most 160 rows go to the four-wave kernel
   int quad_grid;        // its workgroups (two per CU, multiple of 8)
+  int w_paired;         // MXFP4: E2M1 weights in the row-pair layout (one 128-byte line per K block of two rows)
   int wsf_kmajor;       // per-32 recipes: weight scales as [E][K/128][rows] words (4 UE8M0 codes
                         // of one 128-K block of one row), else [E][rows][K/32] bytes
   int inter64;          // FP8 recipe: the intermediate has a float scale per 64 channels, inter_sf
@@ -245,6 +250,7 @@ hipError_t launch_combine(const Args& a, hipStream_t s);
 hipError_t launch_fused(const Args& a, hipStream_t s);
 // out[e][kb][r] = in[e][r][kb] over E experts of `rows` rows and KB words per row (32-bit words)
 hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s);
+hipError_t launch_e2m1_pairs(const uint8_t* in, uint8_t* out, size_t pairs, int KB, hipStream_t s);
 // n_tiles 16 x 16 block dot products with the GEMMs' MFMA (fmt as in mega_moe_diag_mfma_block_sums)
 hipError_t launch_diag_mfma(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
                             float* out, int n_tiles, hipStream_t s);

@@ -98,15 +98,15 @@ template <int R>
 __device__ __forceinline__ void l1_arrive(const Args& a) {
   publish();
   if (threadIdx.x != 0) return;
-  const int n_slabs = large_slabs_of<true>(a), n_tiles = large_tiles_of<R, true>(a);
-  const ItemRounds rs(n_tiles * n_slabs);
-  int items = 0;
+  const ItemSpace sp = item_space<R, true>(a);
+  const ItemRounds rs(sp.count());
+  int items = 0;                                  // in slabs: a wide item counts for two
   for (int r = 0;; ++r) {
     const int q = rs.item(r);
     if (q < 0) break;
-    __hip_atomic_fetch_add(&a.tile_done[item_pos(q, n_slabs, n_tiles).tile], 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    ++items;
+    const ItemPos ip = item_pos(q, sp);
+    __hip_atomic_fetch_add(&a.tile_done[ip.tile], ip.wide ? 2 : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    items += ip.wide ? 2 : 1;
   }
   __hip_atomic_fetch_add(&a.tile_done[a.max_tiles_l], items, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

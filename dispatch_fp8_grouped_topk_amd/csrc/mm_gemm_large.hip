@@ -55,13 +55,6 @@ struct QLds {
 };
 static_assert(sizeof(QLds) <= 80 * 1024, "two workgroups per CU");
 
-// E2M1 operand of one lane (16 bytes): the MFMA reads only the low four registers of an FP4
-// operand, so the upper four are left undefined instead of zeroed (16 VGPRs fewer for the
-// four weight tiles, which the ten-group tiles need).
-__device__ __forceinline__ v8i lds_fp4_operand_lo(const uint8_t* lo, int off) {
-  const v4i a = *reinterpret_cast<const v4i*>(lo + off);
-  return __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
-}
 
 template <int NC>
 __device__ __forceinline__ StageRef qstage_ref(uint8_t* ring, int slot) {
@@ -86,6 +79,7 @@ struct QSrc {
   uint32_t ao, so;
   uint32_t akb, skb;                          // bytes per K block of the two scale sources
   uint32_t wend;                              // bytes of the weight buffer (wr's size)
+  int wkb;                                    // bytes per K block of a weight row (pair)
 };
 
 template <int NC>
@@ -102,7 +96,7 @@ __device__ __forceinline__ void qissue_load(const StageRef& F, const QSrc& s, in
   const int kb = min(kb_, KB - 1);
   if (j < 4) {
     const bool past = kb_ >= KB;
-    lds_load16(s.wr, past ? s.wend : s.wo[j], past ? 0 : kb * 64, F.w + (64 * w + 16 * j) * 64);
+    lds_load16(s.wr, past ? s.wend : s.wo[j], past ? 0 : kb * s.wkb, F.w + (64 * w + 16 * j) * 64);
   } else if (j < 4 + NT) {
     lds_load16(s.xr, s.xo[j - 4], kb * 128, F.x + qtoken_block<NC>(w, j - 4) * 8 * 128);
   } else if (j == 4 + NT) {
@@ -182,11 +176,14 @@ __device__ __forceinline__ void q_loop(QLds& L, const QSrc& src, int arow0, int 
 template <int NC, class F>
 __device__ __forceinline__ void q_offsets(QSrc& s, const int* rowsrc, uint32_t xrow_bytes, F grow,
                                           uint32_t wrow_bytes, uint32_t wsrow_bytes, int off, int cnt, int w,
-                                          int lane) {
+                                          int lane, bool paired) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 64 * w + 16 * j + (lane >> 2);
-    s.wo[j] = (uint32_t)grow(r) * wrow_bytes + 16u * (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    const int g = grow(r);
+    const uint32_t piece = 16u * (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    s.wo[j] = paired ? (uint32_t)(g >> 1) * 2u * wrow_bytes + 64u * (uint32_t)(g & 1) + piece
+                     : (uint32_t)g * wrow_bytes + piece;   // row-pair layout: see weight_offsets
   }
 #pragma unroll
   for (int j = 0; j < kQTokenLoads<NC>; ++j) {
@@ -217,7 +214,8 @@ __device__ __forceinline__ void q_tile(const Args& a, int e, int off, int cnt, i
     const int g = kWRows * slab + (r & ~63) + 16 * (m >> 2) + 4 * rt + (m & 3);
     return g < H ? g : g - 128;
   };
-  q_offsets<NC>(src, L.rowsrc, I, grow, I / 2, a.wsf_kmajor ? 4 : I / 32, off, cnt, w, lane);
+  q_offsets<NC>(src, L.rowsrc, I, grow, I / 2, a.wsf_kmajor ? 4 : I / 32, off, cnt, w, lane, a.w_paired != 0);
+  src.wkb = a.w_paired ? 128 : 64;
   v4f acc[4][NC];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -260,7 +258,7 @@ __global__ __launch_bounds__(kQThreads, 2) void k_quad_l2(Args a) {
   const int mine = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   const int tid = threadIdx.x;
   for (int q = mine; q < n_items; q += G) {
-    const ItemPos ip = item_pos(q, n_slabs, n_tiles);
+    const ItemPos ip = band_pos(q, n_slabs, n_tiles, 0);
     const int2 td = a.tiles_l[t0 + ip.tile];
       const int e = tile_expert(td.x), cnt = tile_rows(td.x), off = td.y;
     lds_barrier();                               // the previous item is done with the LDS

@@ -37,20 +37,29 @@ struct OpLoad;
 // FP8 weight rows: K block kb of a row starts at byte 128*kb.
 template <>
 struct OpLoad<0> {
-  static __device__ __forceinline__ v8i w(const uint8_t* row, int kb, int lg) {
+  static __device__ __forceinline__ v8i w(const uint8_t* row, int kb, int lg, bool) {
     return load_fp8_operand(row + 128 * kb, lg);
   }
 };
 // E4M3 weight rows with per-32 UE8M0 scales: laid out as the FP8 recipe's.
 template <>
 struct OpLoad<2> : OpLoad<0> {};
-// E2M1 weight rows: K block kb starts at byte 64*kb.
+// E2M1 weight rows: K block kb starts at byte 64*kb, or 128*kb in the row-pair layout (the row's
+// offset within the expert from w_row_offset).
 template <>
 struct OpLoad<1> {
-  static __device__ __forceinline__ v8i w(const uint8_t* row, int kb, int lg) {
-    return load_fp4_operand(row + 64 * kb, lg);
+  static __device__ __forceinline__ v8i w(const uint8_t* row, int kb, int lg, bool paired) {
+    return load_fp4_operand(row + (paired ? 128 : 64) * kb, lg);
   }
 };
+
+// Byte offset of weight row `row` within its expert: row-major, or (E2M1 only) the row-pair
+// layout (MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED: rows 2q, 2q + 1 share 128-byte lines, K block by K block).
+template <int R>
+__device__ __forceinline__ size_t w_row_offset(const Args& a, int row, size_t wstride) {
+  if (R == 1 && a.w_paired) return (size_t)(row >> 1) * 2 * wstride + 64 * (row & 1);
+  return (size_t)row * wstride;
+}
 
 // ------------------------------------------------------------------------------------ L1
 template <int R, int NSUB>
@@ -82,7 +91,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int row = (rt < 2 ? 0 : I) + 128 * slab + 32 * w + 16 * (rt & 1) + lr;
-    wrow[rt] = a.l1_w + ((size_t)e * 2 * I + row) * wstride;
+    wrow[rt] = a.l1_w + (size_t)e * 2 * I * wstride + w_row_offset<R>(a, row, wstride);
   }
   const uint8_t* xrow[NSUB];
 #pragma unroll
@@ -96,7 +105,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
 
   v8i A[4], B[NSUB];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) A[rt] = OpLoad<R>::w(wrow[rt], 0, lg);
+  for (int rt = 0; rt < 4; ++rt) A[rt] = OpLoad<R>::w(wrow[rt], 0, lg, a.w_paired != 0);
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) B[s] = load_fp8_operand(xrow[s], lg);
 
@@ -109,7 +118,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
       v8i An[4], Bn[NSUB];
       const int kn = kb + 1 < KB ? kb + 1 : kb;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg);
+      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg, a.w_paired != 0);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(xrow[s] + 128 * kn, lg);
       const float sg = sfg[kb], su = sfu[kb];
@@ -143,7 +152,7 @@ __device__ __forceinline__ void l1_tile(const Args& a, int e, int m0, int cnt, i
       v8i An[4], Bn[NSUB];
       const int kn = kb + 1 < KB ? kb + 1 : kb;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg);
+      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg, a.w_paired != 0);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(xrow[s] + 128 * kn, lg);
       int sw[4];
@@ -289,7 +298,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
   const size_t wstride = R == 1 ? (size_t)I / 2 : (size_t)I;
   const uint8_t* wrow[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) wrow[rt] = a.l2_w + ((size_t)e * H + nbase + 16 * rt + lr) * wstride;
+  for (int rt = 0; rt < 4; ++rt) wrow[rt] = a.l2_w + (size_t)e * H * wstride + w_row_offset<R>(a, nbase + 16 * rt + lr, wstride);
   const uint8_t* qrow[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -305,7 +314,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
 
   v8i A[4], B[NSUB];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) A[rt] = OpLoad<R>::w(wrow[rt], 0, lg);
+  for (int rt = 0; rt < 4; ++rt) A[rt] = OpLoad<R>::w(wrow[rt], 0, lg, a.w_paired != 0);
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) B[s] = load_fp8_operand(qrow[s], lg);
 
@@ -317,7 +326,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
       v8i An[4], Bn[NSUB];
       const int kn = kb + 1 < KB ? kb + 1 : kb;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg);
+      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg, a.w_paired != 0);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(qrow[s] + 128 * kn, lg);
       const float sb = sfw[kb];
@@ -358,7 +367,7 @@ __device__ __forceinline__ void l2_tile(const Args& a, int e, int m0, int cnt, i
       v8i An[4], Bn[NSUB];
       const int kn = kb + 1 < KB ? kb + 1 : kb;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg);
+      for (int rt = 0; rt < 4; ++rt) An[rt] = OpLoad<R>::w(wrow[rt], kn, lg, a.w_paired != 0);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) Bn[s] = load_fp8_operand(qrow[s] + 128 * kn, lg);
       int sw[4];

@@ -62,11 +62,11 @@ constexpr int kWRows = 256;                   // weight rows per tile
 // the ring geometries below are the same with or without it).
 constexpr int kRingBudget = 160 * 1024 - 3 * 1024 - 1024;
 
-template <int R, int NG>
+template <int R, int NG, int WX = 1>
 struct Ring {
-  static constexpr int kWBytes = kWRows * (R == 1 ? 64 : 128);
+  static constexpr int kWBytes = kWRows * WX * (R == 1 ? 64 : 128);
   static constexpr int kXRows = 32 * NG;
-  static constexpr int kTBytes = kXRows * 128 + 2048;
+  static constexpr int kTBytes = kXRows * 128 + 1024 * (1 + WX);
   static constexpr int kFit = kRingBudget / (kWBytes + kTBytes);
   static constexpr bool kSplit = kFit < 3 && 3 * kWBytes + 2 * kTBytes <= kRingBudget;
   static constexpr int kWStages = kSplit ? 3 : (kFit > 4 ? 4 : kFit);
@@ -83,9 +83,9 @@ struct StageRef {
 };
 
 // Weight part of ring slot sw and token part of ring slot st.
-template <int R, int NG>
+template <int R, int NG, int WX = 1>
 __device__ __forceinline__ StageRef stage_ref(uint8_t* ring, int sw, int st) {
-  using G = Ring<R, NG>;
+  using G = Ring<R, NG, WX>;
   uint8_t* t = ring + G::kWStages * G::kWBytes + st * G::kTBytes;
   return StageRef{ring + sw * G::kWBytes, t, reinterpret_cast<uint32_t*>(t + G::kXRows * 128)};
 }
@@ -180,15 +180,20 @@ struct Src {
   int wkb;                                    // bytes per K block of a weight row
   uint32_t wend;                              // bytes of the weight buffer (wr's size)
   uint32_t ckb;                               // bytes per K block of this wave's scale source
+  // wide E2M1 items only: the second scale load (UE8M0 words of weight rows 256 + 64 (w % 4) + lane)
+  rsrc_t cr2;
+  uint32_t co2, ckb2;
 };
 
-template <int R>
-constexpr int kWeightLoads = R == 1 ? 2 : 4;
+template <int R, int WX = 1>
+constexpr int kWeightLoads = R == 1 ? 2 * WX : 4;
+template <int WX>
+constexpr int kScaleLoads = WX;                // wide items: 512 weight-scale words need a second load
 constexpr int kSpreadGroups = 3;              // column groups the stage loads are spread over
 template <int NG>
 constexpr int kTokenLoads = (NG + 1) / 2;
-template <int R, int NG>
-constexpr int kStageLoads = kWeightLoads<R> + kTokenLoads<NG> + 1;
+template <int R, int NG, int WX = 1>
+constexpr int kStageLoads = kWeightLoads<R, WX> + kTokenLoads<NG> + kScaleLoads<WX>;
 
 // 8-row token block of load j of wave w: blocks w + 8j cover the 4 NG blocks of the tile; for
 // odd NG, waves 4-7 have no block left in their last load and fetch wave w-4's again (the same
@@ -206,15 +211,15 @@ __device__ __forceinline__ int token_block(int w, int j) {
 // bw >= KB (the steps past the last block): the weight loads take a lane offset at the end of the
 // buffer, so every lane is out of range and reads zeros into the retired slot without touching
 // memory, and they still count as loads, which keeps the number in flight constant.
-template <int R, int NG, bool NTW>
+template <int R, int NG, bool NTW, int WX = 1>
 __device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int bw, int bt, int w, int j, int KB) {
-  constexpr int NW = kWeightLoads<R>, NT = kTokenLoads<NG>;
-  constexpr bool split = Ring<R, NG>::kSplit;
-  const bool is_w = split ? j > NT : j < NW;
+  constexpr int NW = kWeightLoads<R, WX>, NT = kTokenLoads<NG>, NSC = kScaleLoads<WX>;
+  constexpr bool split = Ring<R, NG, WX>::kSplit;
+  const bool is_w = split ? j >= NT + NSC : j < NW;
   const int jt = split ? j : j - NW;                 // index within the token part
-  const int jw = split ? j - NT - 1 : j;             // index within the weight part
+  const int jw = split ? j - NT - NSC : j;           // index within the weight part
   if (is_w) {
-    uint8_t* dst = R != 1 ? F.w + (32 * w + 8 * jw) * 128 : F.w + (32 * w + 16 * jw) * 64;
+    uint8_t* dst = R != 1 ? F.w + (32 * w + 8 * jw) * 128 : F.w + (32 * WX * w + 16 * jw) * 64;
     const bool past = bw >= KB;
     const uint32_t vo = past ? s.wend : s.wo[jw];
     const int so = past ? 0 : bw * s.wkb;
@@ -222,17 +227,19 @@ __device__ __forceinline__ void issue_load(const StageRef& F, const Src& s, int 
     else lds_load16(s.wr, vo, so, dst);
   } else if (jt < NT) {
     lds_load16(s.xr, s.xo[jt], bt * 128, F.x + token_block<NG>(w, jt) * 8 * 128);
-  } else {
+  } else if (jt == NT) {
     lds_load4(s.cr, s.co, (int)((uint32_t)bt * s.ckb), F.scl + 64 * w);
+  } else {
+    lds_load4(s.cr2, s.co2, (int)((uint32_t)bt * s.ckb2), F.scl + 512 + 64 * (w & 3));
   }
 }
 
 // The stage loads of a K step go out behind the MFMAs of its column groups: after group i,
 // loads [stage_split(i), stage_split(i + 1)).  Issued all at once, a wave stalls in the address
 // unit until the queue has room for them; spread out, the queue drains between groups.
-template <int R, int NG>
+template <int R, int NG, int WX = 1>
 __device__ __forceinline__ constexpr int stage_split(int i) {
-  constexpr int C = kStageLoads<R, NG>, G = NG < kSpreadGroups ? NG : kSpreadGroups;
+  constexpr int C = kStageLoads<R, NG, WX>, G = NG < kSpreadGroups ? NG : kSpreadGroups;
   return i >= G ? C : (C * i + G - 1) / G;
 }
 
@@ -248,18 +255,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // plays the steps before 0), so with one depth NS the later NS - 2 steps' loads, and with
 // NSW = NST + 1 the weight part of block kb + 1 (issued after block kb's token part) and the
 // later NST - 2 steps' loads.
-template <int R, int NG>
-constexpr int kInFlight = Ring<R, NG>::kSplit
-                              ? kWeightLoads<R> + (Ring<R, NG>::kTStages - 2) * kStageLoads<R, NG>
-                              : (Ring<R, NG>::kWStages - 2) * kStageLoads<R, NG>;
+template <int R, int NG, int WX = 1>
+constexpr int kInFlight = Ring<R, NG, WX>::kSplit
+                              ? kWeightLoads<R, WX> + (Ring<R, NG, WX>::kTStages - 2) * kStageLoads<R, NG, WX>
+                              : (Ring<R, NG, WX>::kWStages - 2) * kStageLoads<R, NG, WX>;
 
 // LDS operand addressing.  Every row a lane reads has the same residue mod 16 (lr), so the
 // chunk swizzle is the same for all of them and a lane needs two base offsets per tile (the
 // 16-byte chunks of K [16 lg, +16) and [64 + 16 lg, +16) of its first row); the other rows are
 // constant offsets, folded into the ds_read immediates.  L1 weight tiles rt: rows
 // 32 wm + 16 (rt & 1) (+ 128 for the up tiles rt >= 2); L2: rows 64 wm + 16 rt.
-template <bool L1>
-__device__ __forceinline__ constexpr int a_tile_rows(int rt) { return L1 ? (rt >= 2 ? 128 : 0) + 16 * (rt & 1) : 16 * rt; }
+// Wide E2M1 L1 items (WX = 2, 512 weight rows): tiles rt < 4 are the gate rows 64 wm + 16 rt, the
+// up tiles rt >= 4 the rows 256 further on.
+template <bool L1, int WX = 1>
+__device__ __forceinline__ constexpr int a_tile_rows(int rt) {
+  return L1 ? (rt >= 2 * WX ? 128 * WX : 0) + 16 * (rt & (2 * WX - 1)) : 16 * rt;
+}
 
 __device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* lo, const uint8_t* hi, int off) {
   const v4i a = *reinterpret_cast<const v4i*>(lo + off);
@@ -268,6 +279,13 @@ __device__ __forceinline__ v8i lds_fp8_operand(const uint8_t* lo, const uint8_t*
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
+}
+
+// E2M1 operand of one lane (16 bytes): the MFMA reads only the low four registers of an FP4
+// operand, so the upper four are left undefined instead of zeroed (16 VGPRs fewer per four tiles).
+__device__ __forceinline__ v8i lds_fp4_operand_lo(const uint8_t* lo, int off) {
+  const v4i a = *reinterpret_cast<const v4i*>(lo + off);
+  return __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
 __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
@@ -283,10 +301,12 @@ __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
 // weight-scale block (L.wsc row) of tile rt.  H64 (FP8 L2 with per-64 intermediate scales): each
 // 128-K block is two MFMAs, one per 64-K half of the token operand (the other half zeroed), each
 // promoted with its own activation scale (stage words [0, 256) and [256, 512)).
-template <int R, int NG, bool L1, bool NTW, bool H64 = false>
+template <int R, int NG, bool L1, bool NTW, bool H64 = false, int WX = 1>
 __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const int wsel[4], int KB,
-                                       v4f acc[4][NG], int w, int wn, int lane) {
-  constexpr int NSW = Ring<R, NG>::kWStages, NST = Ring<R, NG>::kTStages;
+                                       v4f acc[4 * WX][NG], int w, int wn, int lane) {
+  static_assert(WX == 1 || (R == 1 && L1 && !H64), "wide items: E2M1 L1 only");
+  constexpr int NSW = Ring<R, NG, WX>::kWStages, NST = Ring<R, NG, WX>::kTStages;
+  constexpr int NA = 4 * WX;                 // weight tiles per wave
   const int lr = lane & 15, lg = lane >> 4;
   const int tsp = tok_scale_pos(wn, lr);
   // lane offsets inside a stage's weight and token tiles
@@ -296,9 +316,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
   const int xrow0 = 16 * wn + lr;
   const int xlo = xrow0 * 128 + 16 * (lg ^ sw7);
   const int xhi = xrow0 * 128 + 16 * ((lg | 4) ^ sw7);
-  int swrow[4];                            // per-32 recipes: scale word index of each weight tile's row
+  int swrow[NA];                           // per-32 recipes: scale word index of each weight tile's row
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1>(rt));
+  for (int rt = 0; rt < NA; ++rt) swrow[rt] = scl_w(arow0 + a_tile_rows<L1, WX>(rt));
   // Prologue: the issue of steps -(NSW - 1) .. -1.  Every step issues its loads without a
   // branch; past the last block the weight loads read zeros (a lane offset at the buffer's end:
   // no memory access) and the token loads a copy of block KB - 1, into the slots of retired blocks
@@ -307,11 +327,11 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 #pragma unroll
   for (int j = -(NSW - 1); j < 0; ++j) {
     const int bt = j + NST - 1, bw = j + NSW - 1;
-    const StageRef F = stage_ref<R, NG>(L.ring, bw, bt < 0 ? 0 : bt);
+    const StageRef F = stage_ref<R, NG, WX>(L.ring, bw, bt < 0 ? 0 : bt);
 #pragma unroll
-    for (int l = 0; l < kStageLoads<R, NG>; ++l) {
-      const bool is_w = Ring<R, NG>::kSplit ? l > kTokenLoads<NG> : l < kWeightLoads<R>;
-      if (is_w || bt >= 0) issue_load<R, NG, NTW>(F, src, bw, min(bt < 0 ? 0 : bt, KB - 1), w, l, KB);
+    for (int l = 0; l < kStageLoads<R, NG, WX>; ++l) {
+      const bool is_w = Ring<R, NG, WX>::kSplit ? l >= kTokenLoads<NG> + kScaleLoads<WX> : l < kWeightLoads<R, WX>;
+      if (is_w || bt >= 0) issue_load<R, NG, NTW, WX>(F, src, bw, min(bt < 0 ? 0 : bt, KB - 1), w, l, KB);
     }
   }
   int wslot = 0, tslot = 0;                // weight / token ring slots of block kb
@@ -326,7 +346,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     pend_s[rt] = 0.f;
   }
   for (int kb = 0; kb < KB; ++kb) {
-    wait_vmcnt<kInFlight<R, NG>>();
+    wait_vmcnt<kInFlight<R, NG, WX>>();
     pipeline_barrier();                    // block kb landed for all waves; block kb-1 retired
     // the weight part of block kb + NSW - 1 and the token part of block kb + NST - 1 go to the
     // slots block kb-1 used.  Their loads are issued behind column group 0's MFMAs: issued
@@ -334,15 +354,15 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // the waves back from their first MFMA.
     const int bw = kb + NSW - 1, bt = min(kb + NST - 1, KB - 1);
     const int fw = wslot == 0 ? NSW - 1 : wslot - 1, ft = tslot == 0 ? NST - 1 : tslot - 1;
-    const StageRef F = stage_ref<R, NG>(L.ring, fw, ft);
+    const StageRef F = stage_ref<R, NG, WX>(L.ring, fw, ft);
     // fetch_part(i) issues the loads due after column group i: all of them after group
     // 0.  (The call sites of the later groups issue nothing, but their scheduling fences shape
     // the group loop's schedule.)
     auto fetch_part = [&](int i) {
 #pragma unroll
-      for (int j = stage_split<R, NG>(i); j < stage_split<R, NG>(i + 1); ++j) issue_load<R, NG, NTW>(F, src, bw, bt, w, j, KB);
+      for (int j = stage_split<R, NG, WX>(i); j < stage_split<R, NG, WX>(i + 1); ++j) issue_load<R, NG, NTW, WX>(F, src, bw, bt, w, j, KB);
     };
-    const StageRef S = stage_ref<R, NG>(L.ring, wslot, tslot);
+    const StageRef S = stage_ref<R, NG, WX>(L.ring, wslot, tslot);
     wslot = wslot + 1 == NSW ? 0 : wslot + 1;
     tslot = tslot + 1 == NST ? 0 : tslot + 1;
     const uint8_t* xl = S.x + xlo;
@@ -350,10 +370,11 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     // Column group 0's operands first and alone (10 LDS reads, so the waits before its MFMAs can
     // count them individually; LDS returns in order); the scales and group 1 follow.
     v8i B = lds_fp8_operand(xl, xh, 0);
-    v8i A[4];
+    v8i A[NA];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < NA; ++rt) {
       if (R != 1) A[rt] = lds_fp8_operand(S.w + wlo, S.w + whi, a_tile_rows<L1>(rt) * 128);
+      else if (WX == 2) A[rt] = lds_fp4_operand_lo(S.w + wlo, a_tile_rows<L1, WX>(rt) * 64);
       else A[rt] = lds_fp4_operand(S.w + wlo, a_tile_rows<L1>(rt) * 64);
     }
     uint32_t sw8[8];                       // activation scale words of column groups 0..NG-1
@@ -450,9 +471,9 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         pend_s[rt] = sp * cw[rt];
       }
     } else {
-      int swv[4];
+      int swv[NA];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) swv[rt] = (S.scl[swrow[rt]] >> (8 * lg)) & 0xFF;
+      for (int rt = 0; rt < NA; ++rt) swv[rt] = (S.scl[swrow[rt]] >> (8 * lg)) & 0xFF;
       read_token_scales();
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
@@ -460,7 +481,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
         if (i + 1 < NG) Bn = lds_fp8_operand(xl, xh, 4096 * (i + 1));
         const int sx = (sw8[i] >> (8 * lg)) & 0xFF;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt][i] = mfma_mx<R>(A[rt], B, acc[rt][i], swv[rt], sx);
+        for (int rt = 0; rt < NA; ++rt) acc[rt][i] = mfma_mx<R>(A[rt], B, acc[rt][i], swv[rt], sx);
         __builtin_amdgcn_sched_barrier(0);
         fetch_part(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -487,7 +508,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
 // h64 (FP8 recipe, L2 with per-64 intermediate scales, [I/64][P] words): K block kb's two halves
 // are scale rows 2 kb and 2 kb + 1; waves 0-3 fetch the first half's words and waves 4-7, which
 // have no weight scales to fetch in this recipe, the second half's into words [256, 512).
-template <int R, int NG, class F>
+template <int R, int NG, int WX = 1, class F>
 __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_t row_bytes, rsrc_t sf_pool,
                                               int P, int off, int cnt, rsrc_t w_sf, F grow,
                                               uint32_t wsrow_bytes, int wskb, int w, int lane, bool h64 = false) {
@@ -507,12 +528,20 @@ __device__ __forceinline__ void token_offsets(Src& s, const int* rowsrc, uint32_
   } else {
     s.co = R != 0 ? (uint32_t)grow(d) * wsrow_bytes : 0u;   // FP8: one word, read by every lane
   }
+  if (WX == 2) {                              // wide items: the words of weight rows 256 .. 511
+    s.cr2 = w_sf;
+    s.ckb2 = (uint32_t)wskb;
+    s.co2 = (uint32_t)grow(256 + d) * wsrow_bytes;
+  }
 }
 
 // Per-lane global offsets of one wave's share of the weight rows; grow(r) maps a tile row to
-// the weight row within the expert.
-template <int R, class F>
-__device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_bytes, int w, int lane) {
+// the weight row within the expert.  paired (E2M1): the row-pair layout, where K block kb of rows
+// 2q, 2q + 1 is the 128 bytes at (q * KB + kb) * 128 (row 2q + 1's half second), so a K block is
+// 128 bytes further on (Src::wkb) and the lanes of a row pair read one whole line.
+template <int R, int WX = 1, class F>
+__device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_bytes, int w, int lane,
+                                               bool paired = false) {
   if (R != 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -521,16 +550,20 @@ __device__ __forceinline__ void weight_offsets(Src& s, F grow, uint32_t row_byte
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 32 * w + 16 * j + (lane >> 2);
-      s.wo[j] = (uint32_t)grow(r) * row_bytes + 16u * (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    for (int j = 0; j < 2 * WX; ++j) {
+      const int r = 32 * WX * w + 16 * j + (lane >> 2);
+      const int g = grow(r);
+      const uint32_t piece = 16u * (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+      s.wo[j] = paired ? (uint32_t)(g >> 1) * 2u * row_bytes + 64u * (uint32_t)(g & 1) + piece
+                       : (uint32_t)g * row_bytes + piece;
     }
-    s.wo[2] = s.wo[3] = 0;
+    if (WX == 1) s.wo[2] = s.wo[3] = 0;
   }
 }
 
 // ------------------------------------------------------------------------------------ L1
-template <int R, int NG, bool NTW>
+// WX = 2: a wide E2M1 item, 256 channels of the intermediate (512 rows of w1) per slab.
+template <int R, int NG, bool NTW, int WX = 1>
 __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int cnt, int slab, Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -539,7 +572,7 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
 
   Src src;
   const size_t wrow_bytes = R == 1 ? (size_t)H / 2 : (size_t)H;
-  src.wkb = R == 1 ? 64 : 128;
+  src.wkb = R == 1 && !a.w_paired ? 64 : 128;
   src.wr = make_rsrc(a.l1_w + (size_t)e * 2 * I * wrow_bytes, 2 * (size_t)I * wrow_bytes);
   src.wend = (uint32_t)(2 * (size_t)I * wrow_bytes);
   src.xr = make_rsrc(a.x, (size_t)a.T * H);
@@ -548,29 +581,38 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
                                 2 * (size_t)I * (H / 32));
   // Gate tile row 32 wm + 16 t + m (and the up tile row 128 further on) holds channel
   // 32 wm + 8 (m / 4) + 4 t + m % 4 of the slab: the lane holding rows 4 lg .. 4 lg + 3 of both
-  // gate tiles then holds 8 consecutive channels of its token, stored as one 8-byte piece.
+  // gate tiles then holds 8 consecutive channels of its token, stored as one 8-byte piece.  Wide
+  // items: gate tile row 64 wm + 16 t + m (up: 256 further on) holds channel
+  // 64 wm + 32 (t / 2) + 8 (m / 4) + 4 (t % 2) + m % 4, so tiles 2p, 2p + 1 of a wave are again
+  // one 32-channel group.
   const auto grow = [&](int r) {
-    const int q = r & 127, m = q & 15;
-    const int c = (q & ~31) + 8 * (m >> 2) + 4 * ((q >> 4) & 1) + (m & 3);
-    return (r < 128 ? 0 : I) + 128 * slab + c;
+    if (WX == 1) {
+      const int q = r & 127, m = q & 15;
+      const int c = (q & ~31) + 8 * (m >> 2) + 4 * ((q >> 4) & 1) + (m & 3);
+      return (r < 128 ? 0 : I) + 128 * slab + c;
+    }
+    const int q = r & 255, m = q & 15, t = (q >> 4) & 3;
+    const int c = (q & ~63) + 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+    return (r < 256 ? 0 : I) + 256 * slab + c;
   };
-  weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
-  token_offsets<R, NG>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : H / 32,
-                       a.wsf_kmajor ? 8 * I : 4, w, lane);
+  weight_offsets<R, WX>(src, grow, (uint32_t)wrow_bytes, w, lane, R == 1 && a.w_paired);
+  token_offsets<R, NG, WX>(src, L.rowsrc, H, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : H / 32,
+                           a.wsf_kmajor ? 8 * I : 4, w, lane);
   int wsel[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) wsel[rt] = rt < 2 ? 0 : 1;
 
-  v4f acc[4][NG];
+  v4f acc[4 * WX][NG];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 4 * WX; ++rt)
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[rt][i] = v4f{0.f, 0.f, 0.f, 0.f};
-  k_loop<R, NG, true, NTW>(L, src, 32 * wm + lr, wsel, KB, acc, w, wn, lane);
+  k_loop<R, NG, true, NTW, false, WX>(L, src, 32 * WX * wm + lr, wsel, KB, acc, w, wn, lane);
 
   // ---------------- epilogue: SwiGLU, clamp, top-k weight, group amax, scale, E4M3 cast
-  // acc[t][i][r] (gate) and acc[2+t][i][r] (up) are channel 32wm + 8lg + 4t + r of the slab
-  // for tile row 16(2i + wn) + lr.
+  // acc[2p + t][i][r] (gate) and acc[2 WX + 2p + t][i][r] (up), p < WX, are channel
+  // 32 WX wm + 32 p + 8 lg + 4 t + r of the slab for tile row 16 (2i + wn) + lr.
+  static_assert(R != 0 || WX == 1, "FP8 items are not wide");
   const bool clamp_in = a.clamp > 0.f && a.clamp_inputs, clamp_out = a.clamp > 0.f && !a.clamp_inputs;
   // FP8: the group amax is reduced across the four row groups through the end of the ring, which
   // other waves may still be reading (their last K block) or filling (copies past the end)
@@ -583,37 +625,41 @@ __device__ __forceinline__ void l1_large_tile(const Args& a, int e, int off, int
     for (int i = 0; i < NG; ++i) {
       const int col = 16 * (2 * i + wn) + lr;
       const float wt = col < cnt ? __int_as_float(L.aux[col]) : 0.f;
-      float am = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int p = 0; p < WX; ++p) {
+        float am = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float g = acc[t][i][r], u = acc[2 + t][i][r];
-          const float sv = swiglu_f32<decltype(precise)::value>(g, u, a.clamp, clamp_in, clamp_out);
-          const float x = sv * wt;
-          v[i][t][r] = x;
-          am = fmaxf(am, fabsf(x));
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float g = acc[2 * p + t][i][r], u = acc[2 * WX + 2 * p + t][i][r];
+            const float sv = swiglu_f32<decltype(precise)::value>(g, u, a.clamp, clamp_in, clamp_out);
+            const float x = sv * wt;
+            v[i][t][r] = x;
+            am = fmaxf(am, fabsf(x));
+          }
+        am = fmaxf(am, __shfl_xor(am, 16, 64));
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        if (R == 0) {
+          if (lg == 0) red[wm][col] = am;
+        } else {
+          // per-32 recipes: the 32-channel group from channel cb is this wave's gate tiles 2p, 2p + 1
+          const int cb = 128 * WX * slab + 32 * WX * wm + 32 * p;
+          const uint32_t code = ue8m0_for_amax(am);
+          const int ex = 127 - (int)code;
+          const bool valid = col < cnt;
+          uint2 q = make_uint2(0u, 0u);
+          if (am > 0.f) {
+            q.x = pack_fp8x4(clamp448(ldexpf(v[i][0][0], ex)), clamp448(ldexpf(v[i][0][1], ex)),
+                             clamp448(ldexpf(v[i][0][2], ex)), clamp448(ldexpf(v[i][0][3], ex)));
+            q.y = pack_fp8x4(clamp448(ldexpf(v[i][1][0], ex)), clamp448(ldexpf(v[i][1][1], ex)),
+                             clamp448(ldexpf(v[i][1][2], ex)), clamp448(ldexpf(v[i][1][3], ex)));
+          }
+          if (valid) *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + cb + 8 * lg) = q;
+          if (valid && lg == 0)
+            static_cast<uint8_t*>(a.inter_sf)[((size_t)(cb >> 7) * a.P + off + col) * 4 + ((cb >> 5) & 3)] =
+                (uint8_t)code;
         }
-      am = fmaxf(am, __shfl_xor(am, 16, 64));
-      am = fmaxf(am, __shfl_xor(am, 32, 64));
-      if (R == 0) {
-        if (lg == 0) red[wm][col] = am;
-      } else {
-        // per-32 recipes: the 32-channel group is this wave's two gate tiles
-        const uint32_t code = ue8m0_for_amax(am);
-        const int ex = 127 - (int)code;
-        const bool valid = col < cnt;
-        uint2 q = make_uint2(0u, 0u);
-        if (am > 0.f) {
-          q.x = pack_fp8x4(clamp448(ldexpf(v[i][0][0], ex)), clamp448(ldexpf(v[i][0][1], ex)),
-                           clamp448(ldexpf(v[i][0][2], ex)), clamp448(ldexpf(v[i][0][3], ex)));
-          q.y = pack_fp8x4(clamp448(ldexpf(v[i][1][0], ex)), clamp448(ldexpf(v[i][1][1], ex)),
-                           clamp448(ldexpf(v[i][1][2], ex)), clamp448(ldexpf(v[i][1][3], ex)));
-        }
-        if (valid)
-          *reinterpret_cast<uint2*>(a.inter_q + (size_t)(off + col) * I + 128 * slab + 32 * wm + 8 * lg) = q;
-        if (valid && lg == 0)
-          static_cast<uint8_t*>(a.inter_sf)[((size_t)slab * a.P + off + col) * 4 + wm] = (uint8_t)code;
       }
     }
   };
@@ -653,7 +699,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
 
   Src src;
   const size_t wrow_bytes = R == 1 ? (size_t)I / 2 : (size_t)I;
-  src.wkb = R == 1 ? 64 : 128;
+  src.wkb = R == 1 && !a.w_paired ? 64 : 128;
   src.wr = make_rsrc(a.l2_w + (size_t)e * H * wrow_bytes, (size_t)H * wrow_bytes);
   src.wend = (uint32_t)((size_t)H * wrow_bytes);
   src.xr = make_rsrc(a.inter_q, (size_t)a.P * I);
@@ -669,7 +715,7 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
     const int g = kWRows * slab + (r & ~63) + 16 * (m >> 2) + 4 * rt + (m & 3);
     return g < H ? g : g - 128;
   };
-  weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane);
+  weight_offsets<R>(src, grow, (uint32_t)wrow_bytes, w, lane, R == 1 && a.w_paired);
   token_offsets<R, NG>(src, L.rowsrc, I, sf_pool, a.P, off, cnt, w_sf, grow, a.wsf_kmajor ? 4 : I / 32,
                        a.wsf_kmajor ? 4 * H : 4, w, lane, H64);
   int wsel[4];
@@ -713,25 +759,39 @@ __device__ __forceinline__ void l2_large_tile(const Args& a, int e, int off, int
 // kBand of its tiles, and each tile's rows once for 32 / kBand slabs.
 constexpr int kBand = 4;
 
-struct ItemPos {
-  int tile, slab;
+// The item list of one GEMM launch: tiles [0, n_norm) in items of one slab, then (wide E2M1 L1
+// items) tiles [n_norm, n_tiles) in items of two slabs, each part numbered in bands as above.
+struct ItemSpace {
+  int n_slabs, n_tiles, n_norm;
+  __device__ __forceinline__ int count() const { return n_norm * n_slabs + (n_tiles - n_norm) * (n_slabs >> 1); }
 };
-__device__ __forceinline__ ItemPos item_pos(int q, int n_slabs, int n_tiles) {
+struct ItemPos {
+  int tile, slab;                               // slab: of the item's own width
+  bool wide;
+};
+__device__ __forceinline__ ItemPos band_pos(int q, int n_slabs, int n_tiles, int t0) {
   const int per_band = kBand * n_slabs;
   const int b = q / per_band, r = q - b * per_band;
   const int in_band = min(kBand, n_tiles - b * kBand);
   const int s = r / in_band;
-  return ItemPos{b * kBand + (r - s * in_band), s};
+  return ItemPos{t0 + b * kBand + (r - s * in_band), s, false};
+}
+__device__ __forceinline__ ItemPos item_pos(int q, const ItemSpace& sp) {
+  const int qn = sp.n_norm * sp.n_slabs;
+  if (q < qn) return band_pos(q, sp.n_slabs, sp.n_norm, 0);
+  ItemPos p = band_pos(q - qn, sp.n_slabs >> 1, sp.n_tiles - sp.n_norm, sp.n_norm);
+  p.wide = true;
+  return p;
 }
 
 // Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
 // The item's tile-list entry is in L.td_next (fetched during the previous item); q_next is the
 // workgroup's next item (-1: none), whose entry this item fetches in turn.
 template <int R, bool L1, bool H64, class Hooks>
-__device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n_slabs, int n_tiles, Lds& L,
+__device__ __forceinline__ void run_item(const Args& a, int q, int q_next, const ItemSpace& sp, Lds& L,
                                          Hooks& hooks) {
   const int tid = threadIdx.x;
-  const ItemPos ip = item_pos(q, n_slabs, n_tiles);
+  const ItemPos ip = item_pos(q, sp);
   const int slab = ip.slab;
   const int H = a.H, I = a.I;
   hooks.before(ip.tile);                        // the fused forward waits here for the tile's inputs
@@ -741,10 +801,11 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   lds_barrier();
   const int2 td = L.td_next;
   const int e = tile_expert(td.x), cnt = tile_rows(td.x), off = td.y;
-  // FP8 weight lines of an expert with one tile are read once: stream them non-temporally (L1;
-  // in L2 only for tiles of at most 32 rows, the pure weight streams: measured, the hint made the
-  // L2 of larger single tiles up to 6% slower while it takes 3-9% off these)
-  const bool nt = R != 1 && tile_single(td.x) && (L1 || cnt <= 32);
+  // Weight lines of an expert with one tile are read once: stream them non-temporally (L1; in L2
+  // only for tiles of at most 32 rows, the pure weight streams: measured, the hint made the L2 of
+  // larger single tiles up to 6% slower while it takes 3-9% off these).  E2M1 weights only in the
+  // row-pair layout: row-major, a K block is half a line, whose other half the next K step reads.
+  const bool nt = (R != 1 || a.w_paired) && tile_single(td.x) && (L1 || cnt <= 32);
   if (tid < kTok) {
     const int pr = off + (tid < cnt ? tid : cnt - 1);
     const int src_pair = a.pool_src[pr];
@@ -774,16 +835,32 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, int n
   // it is older than all of this item's stage loads, so the K loop's first wait covers it
   if (q_next >= 0 && tid < 2)
     lds_load4(make_rsrc(a.tiles_l, (size_t)a.max_tiles_l * 8),
-              (uint32_t)item_pos(q_next, n_slabs, n_tiles).tile * 8u + 4u * tid, 0,
+              (uint32_t)item_pos(q_next, sp).tile * 8u + 4u * tid, 0,
               &L.td_next);
 
   const int nw = ((cnt + 15) / 16 + 1) / 2;    // column groups per wave
+  if (R == 1 && L1 && ip.wide) {                // wide E2M1 L1 items: tiles of at most kWideMaxNG groups per wave
+    switch (nw) {
+#define MM_WCASE(n)                                                    \
+  case n:                                                              \
+    if constexpr (R == 1 && L1) {                                      \
+      if (nt) l1_large_tile<R, n, true, 2>(a, e, off, cnt, slab, L);   \
+      else l1_large_tile<R, n, false, 2>(a, e, off, cnt, slab, L);     \
+    }                                                                  \
+    break;
+      MM_WCASE(1) MM_WCASE(2) MM_WCASE(3) MM_WCASE(4)
+      default: MM_WCASE(5)
+#undef MM_WCASE
+    }
+    hooks.after(ip.tile);
+    return;
+  }
   switch (nw) {
 #define MM_CASE(n)                                                                   \
   case n:                                                                            \
-    if (R != 1 && nt) {                                                              \
-      if (L1) l1_large_tile<R, n, R != 1>(a, e, off, cnt, slab, L);                  \
-      else l2_large_tile<R, n, R != 1, H64>(a, e, off, cnt, slab, L);                \
+    if (nt) {                                                                        \
+      if (L1) l1_large_tile<R, n, true>(a, e, off, cnt, slab, L);                    \
+      else l2_large_tile<R, n, true, H64>(a, e, off, cnt, slab, L);                  \
     } else {                                                                         \
       if (L1) l1_large_tile<R, n, false>(a, e, off, cnt, slab, L);                   \
       else l2_large_tile<R, n, false, H64>(a, e, off, cnt, slab, L);                 \
@@ -846,16 +923,27 @@ __device__ __forceinline__ int large_slabs_of(const Args& a) {
 }
 
 // The persistent item loop of one GEMM over this workgroup's items.
+// The item list of the GEMM.  E2M1 L1 (I a multiple of 256): the tiles of experts whose first
+// tile has at most kWideMaxNG column groups per wave (from hdr[kHdrTilesWide] on in the tile
+// list, which is ordered by that count) run as wide items, 512 rows of w1 each: a K step then
+// does twice the MFMA work behind the same barrier, operand reads of the token tile and scale
+// words, and its fixed costs, while a wave's accumulators (8 tiles x at most 5 groups) still fit.
+template <int R, bool L1>
+__device__ __forceinline__ ItemSpace item_space(const Args& a) {
+  const int n_tiles = large_tiles_of<R, L1>(a);
+  const bool wide = R == 1 && L1 && (a.I % 256) == 0;
+  return ItemSpace{large_slabs_of<L1>(a), n_tiles, wide ? min(a.hdr[kHdrTilesWide], n_tiles) : n_tiles};
+}
+
 template <int R, bool L1, bool H64, class Hooks>
 __device__ __forceinline__ void large_items(const Args& a, Lds& L, Hooks& hooks) {
-  const int n_slabs = large_slabs_of<L1>(a);
-  const int n_tiles = large_tiles_of<R, L1>(a);
-  const ItemRounds rs(n_tiles * n_slabs);
+  const ItemSpace sp = item_space<R, L1>(a);
+  const ItemRounds rs(sp.count());
   int q = rs.item(0);
-  if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[item_pos(q, n_slabs, n_tiles).tile];
+  if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[item_pos(q, sp).tile];
   for (int r = 0; q >= 0; ++r) {
     const int q_next = rs.item(r + 1);
-    run_item<R, L1, H64>(a, q, q_next, n_slabs, n_tiles, L, hooks);
+    run_item<R, L1, H64>(a, q, q_next, sp, L, hooks);
     q = q_next;
   }
 }

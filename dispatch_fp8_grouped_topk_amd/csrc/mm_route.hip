@@ -88,6 +88,30 @@ __global__ __launch_bounds__(256) void k_sf_kmajor(const uint32_t* __restrict__ 
     if (r0 + ox < rows && k0 + k < KB) out[base + (size_t)(k0 + k) * rows + r0 + ox] = tile[ox][k];
 }
 
+// The row-pair layout of E2M1 weights (MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED): row pair q (rows 2q, 2q+1
+// of the row-major [pairs * 2][KB * 64] bytes) becomes [KB][2][64] bytes at q * KB * 128, so each
+// 128-K block of the two rows is one 128-byte line.  One thread per 16-byte piece: reads of a
+// wave cover whole 64-byte row blocks, writes whole 128-byte lines.
+__global__ __launch_bounds__(256) void k_e2m1_pairs(const uint4* __restrict__ in, uint4* __restrict__ out,
+                                                     size_t pairs, int KB) {
+  const size_t n = pairs * (size_t)KB * 8;                    // 16-byte pieces
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t q = i / ((size_t)KB * 8);
+    const int r = (int)(i - q * (size_t)KB * 8);              // piece within the pair's output
+    const int kb = r >> 3, h = (r >> 2) & 1, c = r & 3;
+    out[i] = in[((2 * q + h) * (size_t)KB + kb) * 4 + c];
+  }
+}
+
+hipError_t launch_e2m1_pairs(const uint8_t* in, uint8_t* out, size_t pairs, int KB, hipStream_t s) {
+  const size_t n = pairs * (size_t)KB * 8;
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_e2m1_pairs, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const uint4*>(in),
+                     reinterpret_cast<uint4*>(out), pairs, KB);
+  return hipGetLastError();
+}
+
 hipError_t launch_sf_kmajor(const uint32_t* in, uint32_t* out, int E, int rows, int KB, hipStream_t s) {
   const int row_tiles = (rows + 63) / 64, kb_tiles = (KB + 31) / 32;
   const long blocks = (long)E * row_tiles * kb_tiles;

@@ -176,6 +176,7 @@ __device__ __forceinline__ void route_scan(const Args& a, const ScanLds& S) {
     }
     s_class_base[0] = run;                     // total large tiles
     a.hdr[kHdrTilesQuad] = s_class_base[kQuadMaxNG];   // tiles of the classes above kQuadMaxNG
+    a.hdr[kHdrTilesWide] = s_class_base[kWideMaxNG];   // tiles of the classes above kWideMaxNG
   }
   __syncthreads();
   int carry = 0, carry_s = 0;

@@ -80,8 +80,8 @@ typedef enum {
 /* flags: bits 0-1 select the GEMM tile class (0 = library default, chosen per expert from
    its row count (currently the large-M class for every expert), 1 = small-M class only,
    2 = large-M class only); bit 2 is MEGA_MOE_FLAG_CLAMP_INPUTS, bit 3 MEGA_MOE_FLAG_PRECISE_SILU,
-   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, bit 5 MEGA_MOE_FLAG_INTER_SF64, bit 6 MEGA_MOE_FLAG_FUSED;
-   other bits must be 0. */
+   bit 4 MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR, bit 5 MEGA_MOE_FLAG_INTER_SF64, bit 6 MEGA_MOE_FLAG_FUSED,
+   bit 7 MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED; other bits must be 0. */
 #define MEGA_MOE_FLAG_TILE_AUTO  0u
 #define MEGA_MOE_FLAG_TILE_SMALL 1u
 #define MEGA_MOE_FLAG_TILE_LARGE 2u
@@ -101,6 +101,13 @@ typedef enum {
  * 32-bit words, each the four UE8M0 codes of one row's 128-K block (K = H, rows = 2I for l1_sf;
  * K = I, rows = H for l2_sf).  Same sizes as the row-major layout; the results are identical. */
 #define MEGA_MOE_FLAG_WEIGHT_SF_KMAJOR 16u
+/* flags bit 7 (MEGA_MOE_RECIPE_MXFP4W_B32 only; INVALID_ARG with the other recipes): l1_w and
+ * l2_w are in the row-pair layout that mega_moe_transform_weights() writes: for each pair of
+ * weight rows (2q, 2q + 1) of an expert and each 128-K block kb, the 64 bytes of row 2q's block
+ * followed by the 64 bytes of row 2q + 1's, so one K block of two rows is one 128-byte line
+ * (offset (q * K/128 + kb) * 128 + (row % 2) * 64 within the expert).  Same sizes as the
+ * row-major layout; the results are identical. */
+#define MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED 128u
 /* flags bit 5 (MEGA_MOE_RECIPE_FP8_B128 only; INVALID_ARG with the per-32 recipes): the SM90
  * design's per-64 intermediate scales.  The L1 epilogue re-quantises the SwiGLU output with one
  * float scale amax/448 per 64 channels instead of per 128, and the L2 GEMM sums each 128-K block
@@ -246,6 +253,18 @@ int mega_moe_forward_stats(const mega_moe_problem* p,
    NULL_POINTER; MISALIGNED (16 bytes); UNSUPPORTED_DEVICE; HIP. */
 int mega_moe_transform_weight_scales(const mega_moe_problem* p, const void* l1_sf, const void* l2_sf,
                                      void* l1_sf_kmajor, void* l2_sf_kmajor, void* stream);
+
+/* The MXFP4 recipe's weight transform, run once when the weights are loaded (the same model-load
+   weight re-layout: design page "MegaMoE SM90 Implementation Design", section 15; research report
+   section 6.2).  Reads the row-major E2M1 weights l1_w [E, 2I, H/2] and l2_w [E, H, I/2] bytes and
+   writes them in the row-pair layout of MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED into l1_w_paired and
+   l2_w_paired (caller-allocated, same sizes, distinct from the inputs): a 128-K block of an E2M1
+   row is half a 128-byte line, and in this layout the GEMMs fetch whole lines (and can stream the
+   weights of single-tile experts past the caches).  Enqueued on `stream` (NULL: default stream).
+   Errors: INVALID_ARG for a recipe other than MXFP4W_B32, an invalid problem or overlapping
+   buffers; NULL_POINTER; MISALIGNED (16 bytes); UNSUPPORTED_DEVICE; HIP. */
+int mega_moe_transform_weights(const mega_moe_problem* p, const void* l1_w, const void* l2_w,
+                               void* l1_w_paired, void* l2_w_paired, void* stream);
 
 /* Fill *out with device pointers into `workspace` for problem p (the layout of
    mega_moe_workspace_size; see mega_moe_views).  The views stay valid while the workspace does and

@@ -56,8 +56,11 @@ def run_gpu(spec: synth.Spec, D: dict, flags: int = 0, workspace=None, fill=None
     l1_sf, l2_sf = D["l1_sf"], D["l2_sf"]
     if flags & mm.FLAG_WEIGHT_SF_KMAJOR:          # the one-time weight-scale transform, then its layout
         l1_sf, l2_sf = mm.mega_moe_transform_weight_scales(prob, l1_sf, l2_sf)
-    mm.mega_moe_forward(prob, D["x"], D["x_sf"], D["topk_idx"], D["topk_w"], D["l1_w"], l1_sf,
-                        D["l2_w"], l2_sf, y, workspace)
+    l1_w, l2_w = D["l1_w"], D["l2_w"]
+    if flags & mm.FLAG_WEIGHT_E2M1_PAIRED:        # the one-time E2M1 weight transform, then its layout
+        l1_w, l2_w = mm.mega_moe_transform_weights(prob, l1_w, l2_w)
+    mm.mega_moe_forward(prob, D["x"], D["x_sf"], D["topk_idx"], D["topk_w"], l1_w, l1_sf,
+                        l2_w, l2_sf, y, workspace)
     torch.cuda.synchronize()
     views = mm.mega_moe_workspace_views(prob, workspace) if spec.T > 0 else None
     return y.view(torch.int16), views, workspace

@@ -76,7 +76,9 @@ def test_workspace_size_grows_with_tokens_and_covers_buffers():
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(H=0), dict(I=96), dict(E=0), dict(E=10 ** 6), dict(k=0),
                                 dict(k=65), dict(recipe=3), dict(recipe=-1), dict(clamp=-1.0), dict(clamp=float("nan")),
-                                dict(flags=128), dict(flags=3), dict(flags=15), dict(flags=16), dict(T=-1), dict(H=32768),
+                                dict(flags=256), dict(flags=3), dict(flags=15), dict(flags=16), dict(T=-1), dict(H=32768),
+                                # the row-pair weight layout: E2M1 weights only
+                                dict(flags=128), dict(flags=128, recipe=2),
                                 # the fused forward runs the large-M tiles only
                                 dict(flags=64 | 1),
                                 # per-64 intermediate scales: the float-scale recipe only
@@ -97,6 +99,36 @@ def test_weight_sf_kmajor_flag_only_with_per32_recipes():
     for recipe in (1, 2):
         for flags in (16, 17, 18, 30):
             assert mm.mega_moe_workspace_size(_p(recipe=recipe, clamp=1.0, flags=flags)) > 0
+
+
+def test_weight_e2m1_paired_flag_only_with_mxfp4():
+    for flags in (128, 128 | 16, 128 | 1, 128 | 64):
+        assert mm.mega_moe_workspace_size(_p(recipe=1, flags=flags)) > 0
+
+
+def _transform_w_raw(problem, ptrs):
+    lib = mm.library()
+    args = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return lib.mega_moe_transform_weights(ctypes.byref(problem), *args, None)
+
+
+def test_transform_weights_validates_before_any_device_work():
+    # E2M1 weights of one expert at H = I = 128: l1 16 KiB, l2 8 KiB, at addresses 1 MiB apart;
+    # nothing is dereferenced (see the scale transform's test)
+    small = dict(T=1, H=128, I=128, E=1, k=1)
+    good = [1 << 20, 2 << 20, 3 << 20, 4 << 20]
+    assert _transform_w_raw(_p(recipe=0, **small), good) == -1              # FP8 weights
+    assert _transform_w_raw(_p(recipe=2, **small), good) == -1              # E4M3 weights
+    assert _transform_w_raw(_p(recipe=1, **dict(small, H=100)), good) == -1  # invalid problem
+    for i in range(4):
+        bad = list(good)
+        bad[i] = None
+        assert _transform_w_raw(_p(recipe=1, **small), bad) == -2
+    assert _transform_w_raw(_p(recipe=1, **small), [good[0] + 4] + good[1:]) == -3
+    assert _transform_w_raw(_p(recipe=1, **small), [good[0], good[1], good[0] + 8192, good[3]]) == -1
+    assert _transform_w_raw(_p(recipe=1, **small), [good[0], good[1], good[2], good[1] + 4096]) == -1
+    if not torch.cuda.is_available():
+        assert _transform_w_raw(_p(recipe=1, **small), good) in (-5, -6)   # no device to run on
 
 
 def _transform_raw(problem, ptrs):

@@ -116,4 +116,12 @@ def test_fused_equals_split_at_benchmark_sizes(cfg):
     x, x_sf = synth.make_activations(spec, "cuda")
     P.update(x=x, x_sf=x_sf, topk_idx=idx.cuda(), topk_w=w.cuda())
     flags = mm.FLAG_WEIGHT_SF_KMAJOR if spec.recipe != 0 else 0
+    if spec.recipe == 1:
+        flags |= mm.FLAG_WEIGHT_E2M1_PAIRED
     _same_as_split(spec, P, flags)
+
+
+def test_fused_equals_split_paired_weights():
+    """MXFP4 with row-pair weights (wide L1 items, each counting for two slabs of its tile)."""
+    spec = CASES["mxfp4_shared"]
+    _same_as_split(spec, to_device(synth.make_problem(spec)), mm.FLAG_WEIGHT_E2M1_PAIRED)

@@ -104,11 +104,12 @@ def test_forced_tile_class(name, flags):
     _full_check(spec, synth.make_problem(spec), flags)
 
 
-@pytest.mark.parametrize("flags", [0, 16], ids=["rowmajor_sf", "kmajor_sf"])
+@pytest.mark.parametrize("flags", [0, 16, 16 | 128], ids=["rowmajor_sf", "kmajor_sf", "kmajor_sf_paired_w"])
 def test_mxfp4_every_tile_size(flags):
-    """MXFP4 experts of 1 to 10 row groups of 16 (the four-wave L2 kernel's tile sizes) beside a
-    601-row expert (three tiles of the eight-wave kernel), compared in full, with the weight scales
-    in either layout."""
+    """MXFP4 experts of 1 to 10 row groups of 16 (the four-wave L2 kernel's tile sizes, and the
+    L1 kernel's wide items up to 5 groups per wave) beside a 601-row expert (three tiles of the
+    eight-wave kernel), compared in full, with the weight scales in either layout and the weights
+    row-major or in row pairs."""
     counts = [1, 17, 33, 49, 65, 81, 97, 113, 129, 150, 160, 601]
     T, k = sum(counts) // 2, 2
     ids = np.repeat(np.arange(len(counts)), counts)           # sorted; no expert holds T pairs
@@ -129,6 +130,33 @@ def test_weight_sf_kmajor(name, flags):
     import dispatch_fp8_grouped_topk_amd as mm
     spec = SMALL[name]
     _full_check(spec, synth.make_problem(spec), flags | mm.FLAG_WEIGHT_SF_KMAJOR)
+
+
+# ------------------------------------------------------------------------------ E2M1 row-pair weights
+@pytest.mark.parametrize("flags", [0, 1, 2], ids=["auto", "small_only", "large_only"])
+@pytest.mark.parametrize("name", ["mxfp4", "mxfp4_multi_tile", "mxfp4_clamp_inputs"])
+def test_weight_e2m1_paired(name, flags):
+    """E2M1 weights transformed once (mega_moe_transform_weights) and read in row pairs
+    (MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED), in every tile class: the same bar against the oracle,
+    which reads the row-major originals."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    spec = SMALL[name]
+    _full_check(spec, synth.make_problem(spec), flags | mm.FLAG_WEIGHT_E2M1_PAIRED)
+
+
+def test_e2m1_pair_transform_is_the_documented_permutation():
+    """Row pair q of a [rows, K/2] expert becomes [K/128][2][64] bytes at q * K: K block kb of row
+    2q, then of row 2q + 1 (one and many K blocks; L1 and L2 weights)."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    for H, I, E in ((640, 384, 5), (128, 4352, 2)):
+        spec = synth.Spec(8, H, I, E, 2, recipe=1, seed=136, weight_set=136)
+        _say(f"pair transform {spec}")
+        D = to_device(synth.make_problem(spec))
+        p1, p2 = mm.mega_moe_transform_weights(problem_of(spec), D["l1_w"], D["l2_w"])
+        torch.cuda.synchronize()
+        e1 = D["l1_w"].view(E, I, 2, H // 128, 64).permute(0, 1, 3, 2, 4).reshape(E, 2 * I, H // 2)
+        e2 = D["l2_w"].view(E, H // 2, 2, I // 128, 64).permute(0, 1, 3, 2, 4).reshape(E, H, I // 2)
+        assert torch.equal(p1, e1) and torch.equal(p2, e2)
 
 
 @pytest.mark.parametrize("recipe", [1, 2])
@@ -365,9 +393,20 @@ def test_mxfp8_decode_full_parity():
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_benchmark_config_stratified_parity(cfg):
     """Prefill and MXFP4 workloads at their full sizes on a stratified sample of tokens (every
-    tile of the hottest experts, every column-group class), dispatch in full."""
+    tile of the hottest experts, every column-group class), dispatch in full; MXFP4 with the
+    weight layouts the benchmark uses (K-major scales, row-pair E2M1 weights)."""
     import dispatch_fp8_grouped_topk_amd as mm
-    _parity_at_size(cfg, flags=mm.FLAG_WEIGHT_SF_KMAJOR if cfg == 4 else 0)
+    _parity_at_size(cfg, flags=mm.FLAG_WEIGHT_SF_KMAJOR | mm.FLAG_WEIGHT_E2M1_PAIRED if cfg == 4 else 0)
+
+
+def test_mxfp4_paired_weights_bitwise_at_benchmark_size():
+    """The MXFP4 workload: row-pair E2M1 weights give the same y, bit for bit, as row-major ones
+    (every token)."""
+    import dispatch_fp8_grouped_topk_amd as mm
+    spec, P = _device_problem(4)
+    y0, _, ws = run_gpu(spec, P, mm.FLAG_WEIGHT_SF_KMAJOR)
+    y1, _, _ = run_gpu(spec, P, mm.FLAG_WEIGHT_SF_KMAJOR | mm.FLAG_WEIGHT_E2M1_PAIRED, workspace=ws)
+    assert torch.equal(y0, y1)
 
 
 def test_mxfp4_rowmajor_sf_stratified_parity():

@@ -7,6 +7,8 @@
 // same slab decomposition (L1: one expert x one 128-channel slab, i.e. 256 w1 rows, gate and up;
 // L2: one expert x 256 output columns).  A tile holds up to 256 pool rows of one expert; the
 // route kernel splits an expert's rows into equal tiles of at most 256 (rounded up to 16).
+// E2M1 L1 tiles of at most 5 column groups per wave run as wide items: 256 channels, 512 w1 rows
+// (template parameter WX = 2; see item_space).
 //
 // Workgroup: 8 waves, two per SIMD, so that one wave's LDS reads and promotion arithmetic
 // overlap the other's MFMAs.  Wave w owns weight rows of group wm = w & 3 (64 rows: for L1 two
@@ -50,10 +52,10 @@ constexpr int kTok = kLargeRows;              // pool rows per tile (256)
 constexpr int kWRows = 256;                   // weight rows per tile
 
 // Ring geometry for recipe R and NG column groups per wave.  A stage of block kb has a weight
-// part (the 256 weight rows: 128 bytes of E4M3 or 64 of E2M1 each) and a token part (the first
-// 32 NG token rows, 128 bytes each, and 512 scale words: words [0, 256) are activation scale
-// words in the order (wn, lr, i) of the readers (see tok_scale_row), words [256, 512) the UE8M0
-// scale words (4 x UE8M0) of weight rows 0..255).  The weight parts and the token parts sit in
+// part (the 256 WX weight rows: 128 bytes of E4M3 or 64 of E2M1 each) and a token part (the first
+// 32 NG token rows, 128 bytes each, and 256 + 256 WX scale words: words [0, 256) are activation
+// scale words in the order (wn, lr, i) of the readers (see tok_scale_row), words [256, ...) the
+// UE8M0 scale words (4 x UE8M0) of weight rows 0, 1, ...).  The weight parts and the token parts sit in
 // two rings.  Where three or four whole stages fit in the LDS left beside the per-tile arrays,
 // both rings take that depth; where only two would, the weight ring (streamed from HBM, the
 // loads with the longest latency) takes three and the token ring (rows shared by the slabs of

@@ -55,6 +55,9 @@ SMALL = {
     "mxfp4": synth.Spec(40, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=107, weight_set=107),
     "mxfp4_multi_tile": synth.Spec(200, 512, 256, 3, 2, recipe=1, seed=108, weight_set=108),
     "mxfp4_clamp": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.05, seed=109, weight_set=109),
+    # MXFP4 with I = 768: three wide L1 slabs (256 channels each) under Zipf routing, so experts of
+    # every column-group class up to 5 run wide and the hotter ones in the narrow items
+    "mxfp4_wide3": synth.Spec(400, 512, 768, 16, 4, recipe=1, routing="zipf", seed=137, weight_set=137),
     # the activation clamp on gate and up (flag MEGA_MOE_FLAG_CLAMP_INPUTS)
     "clamp_inputs": synth.Spec(64, 512, 256, 8, 4, routing="biased", swiglu_clamp=0.3, clamp_inputs=True,
                                seed=122, weight_set=122),
@@ -134,7 +137,7 @@ def test_weight_sf_kmajor(name, flags):
 
 # ------------------------------------------------------------------------------ E2M1 row-pair weights
 @pytest.mark.parametrize("flags", [0, 1, 2], ids=["auto", "small_only", "large_only"])
-@pytest.mark.parametrize("name", ["mxfp4", "mxfp4_multi_tile", "mxfp4_clamp_inputs"])
+@pytest.mark.parametrize("name", ["mxfp4", "mxfp4_multi_tile", "mxfp4_clamp_inputs", "mxfp4_wide3"])
 def test_weight_e2m1_paired(name, flags):
     """E2M1 weights transformed once (mega_moe_transform_weights) and read in row pairs
     (MEGA_MOE_FLAG_WEIGHT_E2M1_PAIRED), in every tile class: the same bar against the oracle,

@@ -13,7 +13,7 @@ template <int R, bool L1, bool H64 = false>
 __global__ __launch_bounds__(kThreads) void k_large(Args a) {
   __shared__ __attribute__((aligned(1024))) Lds L;
   NoHooks hooks;
-  large_items<R, L1, H64>(a, L, hooks);
+  large_items<R, L1, H64, true>(a, L, hooks);
 }
 
 // ------------------------------------------------------------------------------ four-wave kernel

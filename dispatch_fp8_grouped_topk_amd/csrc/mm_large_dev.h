@@ -786,6 +786,9 @@ __device__ __forceinline__ ItemPos item_pos(int q, const ItemSpace& sp) {
   return p;
 }
 
+// Column groups per wave of a tile of `rows` pool rows (two waves share its 16-row groups).
+__device__ __forceinline__ int tile_ng(int rows) { return ((rows + 15) / 16 + 1) / 2; }
+
 // Per-item set-up shared by L1 and L2: tile rows, their sources, the FP8 weight-block scales.
 // The item's tile-list entry is in L.td_next (fetched during the previous item); q_next is the
 // workgroup's next item (-1: none), whose entry this item fetches in turn.
@@ -840,7 +843,7 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, const
               (uint32_t)item_pos(q_next, sp).tile * 8u + 4u * tid, 0,
               &L.td_next);
 
-  const int nw = ((cnt + 15) / 16 + 1) / 2;    // column groups per wave
+  const int nw = tile_ng(cnt);                 // column groups per wave
   if (R == 1 && L1 && ip.wide) {                // wide E2M1 L1 items: tiles of at most kWideMaxNG groups per wave
     switch (nw) {
 #define MM_WCASE(n)                                                    \
@@ -891,27 +894,99 @@ struct NoHooks {
 // side (the weight stream of the cheap items overlaps the MFMA work of the costly ones) and every
 // workgroup alternates between them.  Slot `mine` is XCD-major, so each XCD still takes
 // consecutive items.
+// The last round is usually partial (T < G items).  With `balanced` set (balance_last_round),
+// its items go to the T workgroups with the least work in the full rounds instead.
 struct ItemRounds {
-  int n_items, n_front, n_back, half, k0, rounds;
+  int n_items, n_front, n_back, half, k0, rounds, mine;
   bool first_half;
+  bool balanced = false;
+  int last_item = -1;                           // balanced: this workgroup's item of the last round
   __device__ __forceinline__ ItemRounds(int n) : n_items(n) {
     const int G = gridDim.x, per = G >> 3;
     half = G >> 1;
-    const int mine = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    mine = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     n_front = (n_items + 1) >> 1;
     n_back = n_items - n_front;
     first_half = mine < half;
     k0 = first_half ? mine : mine - half;
     rounds = (n_front + half - 1) / half;
   }
-  // item of round r, -1 if none (once a round has none, no later round has one)
-  __device__ __forceinline__ int item(int r) const {
+  // item of slot m in round r of the unbalanced order, -1 if none
+  __device__ __forceinline__ int slot_item(int m, int r) const {
     if (r >= rounds) return -1;
-    const int k = r * half + k0;
-    if (first_half == ((r & 1) == 0)) return k < n_front ? k : -1;
+    const bool fh = m < half;
+    const int k = r * half + (fh ? m : m - half);
+    if (fh == ((r & 1) == 0)) return k < n_front ? k : -1;
     return k < n_back ? n_items - 1 - k : -1;
   }
+  // item of round r, -1 if none (once a round has none, no later round has one)
+  __device__ __forceinline__ int item(int r) const {
+    if (balanced && r == rounds - 1) return last_item;
+    return slot_item(mine, r);
+  }
 };
+
+// Relative cost of an item with ng column groups per wave (wide: two slabs), fitted to per-item
+// traces of the benchmark workloads: the weight stream sets a floor shared by all tiles, and
+// each column group beyond the first adds MFMA and epilogue work, more in L1 (longer K, SwiGLU
+// epilogue) than in L2.
+__device__ __forceinline__ int item_cost(int ng, bool wide, bool l1) {
+  const int c = 40 + (l1 ? 3 : 1) * max(0, 2 * ng - 3);
+  return wide ? 2 * c : c;
+}
+constexpr int kBalanceMaxTiles = 32768;         // tiles whose costs fit the LDS scratch
+
+// Balance the last, partial round (T < G items; rounds - 1 >= 1 full rounds before it).  Every
+// workgroup computes the modelled work of every slot in the full rounds (item_cost of its items),
+// ranks the slots by (work, slot), and the slot of rank j < T takes the j-th item of the last
+// round.  Those items are the T consecutive items from (rounds - 1) * G / 2 on (the middle of the
+// list, where front and back meet), so every item is still taken exactly once.  Called by every
+// thread of the workgroup before its first item, with the ring as scratch; returns this
+// workgroup's item of the last round (-1: none), or -2 to keep the rounds as they are (no partial
+// round, too many tiles for the scratch, or every tile of the same cost: the tile list is ordered
+// by column groups, so first and last tile agree).  Not inlined, so that its registers do not
+// weigh on the item loop's allocation.
+__device__ __noinline__ int balanced_last_item(const int2* tiles, int n_tiles, int n_norm, int n_slabs,
+                                               int n_items, bool l1, uint8_t* ring) {
+  const ItemSpace sp{n_slabs, n_tiles, n_norm};
+  const ItemRounds rs(n_items);
+  const int G = gridDim.x, r_last = rs.rounds - 1;
+  const int T = n_items - r_last * G;
+  if (r_last < 1 || T <= 0 || T >= G || G > kThreads || n_tiles > kBalanceMaxTiles) return -2;
+  // (values read from memory or LDS pass through readfirstlane: the compiler then knows them to
+  // be wave-uniform)
+  const int x_first = __builtin_amdgcn_readfirstlane(tiles[0].x);
+  const int x_last = __builtin_amdgcn_readfirstlane(tiles[n_tiles - 1].x);
+  if (tile_ng(tile_rows(x_first)) == tile_ng(tile_rows(x_last)) && n_norm == n_tiles) return -2;
+  uint8_t* cost = ring;                                            // per tile
+  uint32_t* work = reinterpret_cast<uint32_t*>(ring + kBalanceMaxTiles);   // per slot
+  int* per_wave = reinterpret_cast<int*>(work + kThreads);
+  const int tid = threadIdx.x;
+  for (int t = tid; t < n_tiles; t += kThreads) cost[t] = (uint8_t)item_cost(tile_ng(tile_rows(tiles[t].x)), false, l1);
+  __syncthreads();
+  if (tid < G) {
+    uint32_t s = 0;
+    for (int r = 0; r < r_last; ++r) {
+      const ItemPos ip = item_pos(rs.slot_item(tid, r), sp);
+      s += (uint32_t)cost[ip.tile] * (ip.wide ? 2u : 1u);
+    }
+    work[tid] = s;
+  }
+  __syncthreads();
+  // rank of this slot: the slots before it in (work, slot) order, counted per wave (in the
+  // scratch: no LDS variable of its own, the ring stays the kernel's only LDS object)
+  const uint32_t my = work[rs.mine];
+  const bool before = tid < G && (work[tid] < my || (work[tid] == my && tid < rs.mine));
+  const unsigned long long bal = __ballot(before);
+  if ((tid & 63) == 0) per_wave[tid >> 6] = __popcll(bal);
+  __syncthreads();
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) rank += per_wave[i];
+  __syncthreads();                              // scratch reads done before the first item's loads
+  rank = __builtin_amdgcn_readfirstlane(rank);
+  return rank < T ? r_last * rs.half + rank : -1;
+}
 
 // Large-M tiles of the GEMM (with the four-wave kernel on, the MXFP4 L2 tiles from
 // hdr[kHdrTilesQuad] on are left to it) and slabs per tile.
@@ -937,10 +1012,19 @@ __device__ __forceinline__ ItemSpace item_space(const Args& a) {
   return ItemSpace{large_slabs_of<L1>(a), n_tiles, wide ? min(a.hdr[kHdrTilesWide], n_tiles) : n_tiles};
 }
 
-template <int R, bool L1, bool H64, class Hooks>
+// kBalance: balance the last round (the stand-alone kernels; the fused forward replays the plain
+// rounds to count its L1 arrivals).
+template <int R, bool L1, bool H64, bool kBalance = false, class Hooks>
 __device__ __forceinline__ void large_items(const Args& a, Lds& L, Hooks& hooks) {
   const ItemSpace sp = item_space<R, L1>(a);
-  const ItemRounds rs(sp.count());
+  ItemRounds rs(sp.count());
+  if (kBalance) {
+    const int last = balanced_last_item(a.tiles_l, sp.n_tiles, sp.n_norm, sp.n_slabs, sp.count(), L1, L.ring);
+    if (last != -2) {
+      rs.balanced = true;
+      rs.last_item = last;
+    }
+  }
   int q = rs.item(0);
   if (q >= 0 && threadIdx.x == 0) L.td_next = a.tiles_l[item_pos(q, sp).tile];
   for (int r = 0; q >= 0; ++r) {

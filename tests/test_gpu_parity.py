@@ -361,12 +361,23 @@ def _stratified_tokens(spec, idx):
     return sorted(pick), classes
 
 
+def _assert_every_item_written(spec, y, views, n_rows):
+    """With the workspace filled with 0xFF bytes before the forward (E4M3 NaN codes, BF16 NaNs),
+    every intermediate code of the n_rows pool rows and every output must have been written by
+    the GEMM items: an item left out of the persistent kernels' rounds leaves NaN codes in its
+    slab of the intermediate (L1) or NaN slot rows that reach y through the combine (L2)."""
+    assert torch.isfinite(y.view(torch.bfloat16)).all(), f"{spec.name}: non-finite outputs"
+    q = views["inter_q"][:n_rows]
+    assert not ((q & 0x7F) == 0x7F).any(), f"{spec.name}: intermediate codes left unwritten"
+
+
 def _parity_at_size(cfg, recipe=None, flags=0, full=False, sf64=False):
     spec, P = _device_problem(cfg, recipe=recipe, sf64=sf64)
     _say(f"config {cfg} recipe {spec.recipe} flags {flags}: {spec.name}")
-    y, views, _ = run_gpu(spec, P, flags)
+    y, views, _ = run_gpu(spec, P, flags, fill=0xFF)
     idx = P["topk_idx"].cpu().numpy()
     d = assert_dispatch_exact(spec, idx, views)
+    _assert_every_item_written(spec, y, views, int(d["offset"][-1]))
     if full:
         toks, classes = list(range(spec.T)), None
     else:

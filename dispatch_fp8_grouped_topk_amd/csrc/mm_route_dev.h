@@ -151,37 +151,11 @@ __device__ __forceinline__ void route_scan(const Args& a, const ScanLds& S) {
     if (a.tile_mode == 2) return c > 0;
     return c > 0 && c >= a.large_min_rows;
   };
-  if (tid == 0)
-    for (int g = 0; g <= kMaxNGClasses; ++g) s_class_base[g] = 0;
-  __syncthreads();
-  for (int e0 = 0; e0 < E; e0 += NT) {         // tiles per class
-    const int e = e0 + tid;
-    const int c = e < E ? s_count[e] : 0;
-    const int ntl = large_of(c) ? large_tiles(c) : 0;
-    const int cls = ntl ? large_first_ng(c) : 0;
-    int v[kMaxNGClasses], tot[kMaxNGClasses];
-#pragma unroll
-    for (int g = 0; g < kMaxNGClasses; ++g) v[g] = cls == g + 1 ? ntl : 0;
-    block_scan_n<kMaxNGClasses, NT>(v, sh, tot);
-    if (tid == 0)
-      for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tot[g - 1];
-  }
-  __syncthreads();
-  if (tid == 0) {                              // class g starts after all classes above g
-    int run = 0;
-    for (int g = kMaxNGClasses; g >= 1; --g) {
-      const int n = s_class_base[g];
-      s_class_base[g] = run;
-      run += n;
-    }
-    s_class_base[0] = run;                     // total large tiles
-    a.hdr[kHdrTilesQuad] = s_class_base[kQuadMaxNG];   // tiles of the classes above kQuadMaxNG
-    a.hdr[kHdrTilesWide] = s_class_base[kWideMaxNG];   // tiles of the classes above kWideMaxNG
-  }
-  __syncthreads();
-  int carry = 0, carry_s = 0;
-  for (int e0 = 0; e0 < E; e0 += NT) {
-    const int e = e0 + tid;
+  int carry = 0, carry_s = 0, carry_l = 0;
+  if (E <= NT) {
+    // one expert per thread: one scan of the counts, small tiles and large tiles per class gives
+    // the offsets, the tile positions and, from the class totals, the class bases
+    const int e = tid;
     const int c = e < E ? s_count[e] : 0;
     const bool large = large_of(c);
     const int nts = large ? 0 : (c + kSmallRows - 1) / kSmallRows;
@@ -193,29 +167,100 @@ __device__ __forceinline__ void route_scan(const Args& a, const ScanLds& S) {
 #pragma unroll
     for (int g = 0; g < kMaxNGClasses; ++g) v[2 + g] = cls == g + 1 ? ntl : 0;
     block_scan_n<kMaxNGClasses + 2, NT>(v, sh, tv);
-    const int inc = v[0], tot = tv[0], inc_s = v[1], tot_s = tv[1];
-    int bl = 0;
-    if (cls > 0) bl = s_class_base[cls] + v[1 + cls] - ntl;
-    __syncthreads();
-    if (tid == 0)
-      for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tv[1 + g];
-    __syncthreads();
+    // class g starts after all classes above g
+    int bl = 0, run = 0, base_quad = 0, base_wide = 0;
+#pragma unroll
+    for (int g = kMaxNGClasses; g >= 1; --g) {
+      if (g == cls) bl = run + v[1 + g] - ntl;
+      if (g == kQuadMaxNG) base_quad = run;
+      if (g == kWideMaxNG) base_wide = run;
+      run += tv[1 + g];
+    }
     if (e < E) {
       a.count[e] = c;
       if (a.recv_stats) a.recv_stats[e] += c;
-      a.offset[e] = carry + inc - c;
-      const int bs = carry_s + inc_s - nts;
+      a.offset[e] = v[0] - c;
+      const int bs = v[1] - nts;
       for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);
       for (int i = 0; i < ntl; ++i) {
         const int m0 = large_tile_start(c, i);
         const int m1 = i + 1 < ntl ? large_tile_start(c, i + 1) : c;
-        a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16) | (ntl == 1 ? kTileSingle : 0), carry + inc - c + m0);
+        a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16) | (ntl == 1 ? kTileSingle : 0), v[0] - c + m0);
       }
     }
-    carry += tot;
-    carry_s += tot_s;
+    if (tid == 0) {
+      a.hdr[kHdrTilesQuad] = base_quad;        // tiles of the classes above kQuadMaxNG
+      a.hdr[kHdrTilesWide] = base_wide;        // tiles of the classes above kWideMaxNG
+    }
+    carry = tv[0];
+    carry_s = tv[1];
+    carry_l = run;
+  } else {                                     // experts in several passes of NT
+    if (tid == 0)
+      for (int g = 0; g <= kMaxNGClasses; ++g) s_class_base[g] = 0;
+    __syncthreads();
+    for (int e0 = 0; e0 < E; e0 += NT) {         // tiles per class
+      const int e = e0 + tid;
+      const int c = e < E ? s_count[e] : 0;
+      const int ntl = large_of(c) ? large_tiles(c) : 0;
+      const int cls = ntl ? large_first_ng(c) : 0;
+      int v[kMaxNGClasses], tot[kMaxNGClasses];
+#pragma unroll
+      for (int g = 0; g < kMaxNGClasses; ++g) v[g] = cls == g + 1 ? ntl : 0;
+      block_scan_n<kMaxNGClasses, NT>(v, sh, tot);
+      if (tid == 0)
+        for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tot[g - 1];
+    }
+    __syncthreads();
+    if (tid == 0) {                              // class g starts after all classes above g
+      int run = 0;
+      for (int g = kMaxNGClasses; g >= 1; --g) {
+        const int n = s_class_base[g];
+        s_class_base[g] = run;
+        run += n;
+      }
+      s_class_base[0] = run;                     // total large tiles
+      a.hdr[kHdrTilesQuad] = s_class_base[kQuadMaxNG];   // tiles of the classes above kQuadMaxNG
+      a.hdr[kHdrTilesWide] = s_class_base[kWideMaxNG];   // tiles of the classes above kWideMaxNG
+    }
+    __syncthreads();
+    for (int e0 = 0; e0 < E; e0 += NT) {
+      const int e = e0 + tid;
+      const int c = e < E ? s_count[e] : 0;
+      const bool large = large_of(c);
+      const int nts = large ? 0 : (c + kSmallRows - 1) / kSmallRows;
+      const int ntl = large ? large_tiles(c) : 0;
+      const int cls = ntl ? large_first_ng(c) : 0;
+      int v[kMaxNGClasses + 2], tv[kMaxNGClasses + 2];
+      v[0] = c;
+      v[1] = nts;
+#pragma unroll
+      for (int g = 0; g < kMaxNGClasses; ++g) v[2 + g] = cls == g + 1 ? ntl : 0;
+      block_scan_n<kMaxNGClasses + 2, NT>(v, sh, tv);
+      const int inc = v[0], tot = tv[0], inc_s = v[1], tot_s = tv[1];
+      int bl = 0;
+      if (cls > 0) bl = s_class_base[cls] + v[1 + cls] - ntl;
+      __syncthreads();
+      if (tid == 0)
+        for (int g = 1; g <= kMaxNGClasses; ++g) s_class_base[g] += tv[1 + g];
+      __syncthreads();
+      if (e < E) {
+        a.count[e] = c;
+        if (a.recv_stats) a.recv_stats[e] += c;
+        a.offset[e] = carry + inc - c;
+        const int bs = carry_s + inc_s - nts;
+        for (int i = 0; i < nts; ++i) a.tiles_s[bs + i] = make_int2(e, i * kSmallRows);
+        for (int i = 0; i < ntl; ++i) {
+          const int m0 = large_tile_start(c, i);
+          const int m1 = i + 1 < ntl ? large_tile_start(c, i + 1) : c;
+          a.tiles_l[bl + i] = make_int2(e | ((m1 - m0) << 16) | (ntl == 1 ? kTileSingle : 0), carry + inc - c + m0);
+        }
+      }
+      carry += tot;
+      carry_s += tot_s;
+    }
+    carry_l = s_class_base[0];
   }
-  const int carry_l = s_class_base[0];
   // ids >= E over all dispatch blocks: every thread sums a strided share of the per-block counts
   // (independent loads in flight), then one workgroup reduction
   int inv = 0;

@@ -196,6 +196,13 @@ def test_size_limits_full_parity(name):
     _full_check(spec, synth.make_problem(spec))
 
 
+def test_dispatch_many_blocks():
+    """80,000 pairs in 313 dispatch blocks (a block range of 78-79 blocks per part of the scan's
+    first phase, a ragged last block), every token against the oracle."""
+    spec = synth.Spec(20000, 128, 128, 64, 4, seed=138, weight_set=138)
+    _full_check(spec, synth.make_problem(spec))
+
+
 def test_all_tokens_on_one_expert():
     spec = synth.Spec(150, 512, 256, 8, 1, seed=110, weight_set=110)
     _full_check(spec, _custom(spec, idx=np.full((150, 1), 5)))

@@ -52,6 +52,10 @@ SMALL = {
     "zipf": synth.Spec(512, 512, 384, 32, 4, routing="zipf", seed=104, weight_set=104),
     "T1": synth.Spec(1, 512, 256, 8, 2, seed=105, weight_set=105),
     "E1_k1": synth.Spec(70, 384, 256, 1, 1, seed=106, weight_set=106),
+    # about five rows per expert: four rounds of one-column-group L1 items and two of L2 items (the
+    # decode regime at a small size; FP8 and E4M3-weight per-32 recipes)
+    "decode_like": synth.Spec(160, 512, 512, 256, 8, seed=139, weight_set=139),
+    "decode_like_mxfp8": synth.Spec(160, 512, 512, 256, 8, recipe=2, seed=140, weight_set=140),
     "mxfp4": synth.Spec(40, 512, 256, 9, 5, recipe=1, routing="uniform_shared", seed=107, weight_set=107),
     "mxfp4_multi_tile": synth.Spec(200, 512, 256, 3, 2, recipe=1, seed=108, weight_set=108),
     "mxfp4_clamp": synth.Spec(48, 640, 384, 6, 3, recipe=1, swiglu_clamp=0.05, seed=109, weight_set=109),

@@ -98,7 +98,7 @@ struct Lds {
   uint8_t ring[kRingBytes];
   int rowsrc[kTok];                           // source row of each tile row (token or pool row)
   int aux[kTok];                              // L1: top-k weight (f32 bits) / L2: slot row, per tile row
-  float wsc[2][kMaxKBlocks];                  // FP8 recipe: weight-block scales per K block
+  float wsc[2 * kMaxKBlocks];                 // FP8 recipe: weight-block scale of row block b, K block kb at b KB + kb
   int2 td_next;                               // tile-list entry of the workgroup's next item
   // the fused forward's own variables (unused by the stand-alone kernels).  They live inside this
   // one LDS object on purpose: with a second LDS variable in the kernel the compiler can no longer
@@ -300,7 +300,7 @@ __device__ __forceinline__ v8i lds_fp4_operand(const uint8_t* lo, int off) {
 
 // The K loop shared by L1 and L2 for a wave with NG column groups: acc[rt][i] (+)= weight tile
 // rt x column group 2i + wn.  arow0: the lane's LDS row of weight tile 0; wsel[rt]: the FP8
-// weight-scale block (L.wsc row) of tile rt.  H64 (FP8 L2 with per-64 intermediate scales): each
+// weight-scale row block (of L.wsc) of tile rt.  H64 (FP8 L2 with per-64 intermediate scales): each
 // 128-K block is two MFMAs, one per 64-K half of the token operand (the other half zeroed), each
 // promoted with its own activation scale (stage words [0, 256) and [256, 512)).
 template <int R, int NG, bool L1, bool NTW, bool H64 = false, int WX = 1>
@@ -391,7 +391,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
     if (R == 0 && H64) {
       float cw[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
+      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt] * KB + kb];
       read_token_scales();                 // first-half scales
       uint32_t sh8[8];                     // second-half scales of column groups 0..NG-1
       {
@@ -438,7 +438,7 @@ __device__ __forceinline__ void k_loop(Lds& L, const Src& src, int arow0, const 
       __builtin_amdgcn_sched_barrier(0);
       float cw[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt]][kb];
+      for (int rt = 0; rt < 4; ++rt) cw[rt] = L.wsc[wsel[rt] * KB + kb];
       read_token_scales();
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt][NG - 1] += pend[rt] * pend_s[rt];
@@ -811,28 +811,38 @@ __device__ __forceinline__ void run_item(const Args& a, int q, int q_next, const
   // larger single tiles up to 6% slower while it takes 3-9% off these).  E2M1 weights only in the
   // row-pair layout: row-major, a K block is half a line, whose other half the next K step reads.
   const bool nt = (R != 1 || a.w_paired) && tile_single(td.x) && (L1 || cnt <= 32);
-  if (tid < kTok) {
-    const int pr = off + (tid < cnt ? tid : cnt - 1);
-    const int src_pair = a.pool_src[pr];
-    L.rowsrc[tid] = L1 ? src_pair / a.k : pr;
-    L.aux[tid] = L1 ? __float_as_int(a.w_pool[pr]) : src_pair;
-  }
-  if (R == 0) {
-    if (L1) {
+  if (L1) {
+    if (tid < kTok) {
+      const int pr = off + (tid < cnt ? tid : cnt - 1);
+      const int src_pair = a.pool_src[pr];
+      L.rowsrc[tid] = src_pair / a.k;
+      L.aux[tid] = __float_as_int(a.w_pool[pr]);
+    }
+    if (R == 0) {
       // float scales of the gate block (row 0) and the up block (row 1) for every K block
       const int KB = H / 128;
       const float* sfw = static_cast<const float*>(a.l1_sf) + (size_t)e * (2 * I / 128) * KB;
       for (int i = tid; i < 2 * KB; i += kThreads)
-        L.wsc[i / KB][i % KB] = sfw[(size_t)(i < KB ? slab : I / 128 + slab) * KB + i % KB];
-    } else {
-      // float scales of the slab's two 128-row blocks of w2 (clamped past H) for every K block
-      const int KB = I / 128;
-      const float* sfw = static_cast<const float*>(a.l2_sf) + (size_t)e * (H / 128) * KB;
-      for (int i = tid; i < 2 * KB; i += kThreads) {
-        int blk = 2 * slab + i / KB;
-        blk = blk < H / 128 ? blk : H / 128 - 1;
-        L.wsc[i / KB][i % KB] = sfw[(size_t)blk * KB + i % KB];
-      }
+        L.wsc[i] = sfw[(size_t)(i < KB ? slab : I / 128 + slab) * KB + i % KB];
+    }
+  } else {
+    // L2: the tile rows are pool rows (no load), and the slot rows (waves 0-3) and the FP8 weight
+    // scales of the slab's two 128-row blocks of w2, clamped past H (waves 4-7), go to LDS by
+    // LDS-direct loads: the K loop's first wait covers them, so the set-up waits on no load, nor
+    // on the previous item's output stores ahead of them in the same counter
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // (a scalar branch per wave)
+    if (wv < kTok / 64) {
+      const int pr = off + (tid < cnt ? tid : cnt - 1);
+      L.rowsrc[tid] = pr;
+      lds_load4(make_rsrc(a.pool_src, (size_t)a.P * 4), 4u * (uint32_t)pr, 0, &L.aux[64 * wv]);
+    } else if (R == 0) {
+      const int KB = I / 128, i = tid - kTok;    // 2 KB <= 256 scales: one per lane of waves 4-7
+      int blk = 2 * slab + i / KB;
+      blk = blk < H / 128 ? blk : H / 128 - 1;
+      const uint8_t* sfw = static_cast<const uint8_t*>(a.l2_sf) +
+                           (size_t)__builtin_amdgcn_readfirstlane(e) * (H / 128) * KB * 4;   // uniform: no waterfall
+      lds_load4(make_rsrc(sfw, (size_t)(H / 128) * KB * 4), i < 2 * KB ? 4u * (uint32_t)(blk * KB + i % KB) : ~0u,
+                0, &L.wsc[64 * (wv - kTok / 64)]);
     }
   }
   lds_barrier();
